@@ -1,0 +1,323 @@
+"""Benchmark of the ROCmFP4 hot path on one MI355X.
+
+A step is one decode GEMV over the up-projection workload: dual-scale ROCmFP4 weight
+17408 x 5120 (50,135,040 packed bytes), fp16 activations, batch 1, fp32 output.
+`value` is whole-job GB/s over the timed steps (algorithmic bytes: packed weights +
+activations + outputs) with every input resident in HBM before timing starts. The
+steps rotate over enough distinct weight copies (>= 600 MB) that no step is served
+from the 256 MB Infinity Cache. The K steps are captured once in a HIP graph and
+replayed inside the timed region, bracketed by device synchronizations.
+
+Also measured in the same run (reported under "gemm" and "extra"): the prefill GEMM
+(2048 x 17408 x 5120, bf16, TFLOP/s), the fast-layout down-projection GEMV at batch
+1/2/4/8 (bf16), dequantization, and the 64-layer decode sweep (448 GEMVs, 12.3 GB).
+Per-kernel durations come from HIP events recorded around every launch on the stream
+the kernel runs on. The CPU baseline times the fp64 oracle on the host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-sweep]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ROCmFP4 GEMV GB/s (% of HBM peak) at 5120×17408 b=1; prefill GEMM TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROTATE_MIN_BYTES = 600 * 2**20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_up.json")
+GEMV_SOURCES = ["gemm_rfp4_block_amd/csrc/gemv.hip", "gemm_rfp4_block_amd/csrc/rfp4_decode.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stats_us(samples_ms):
+    a = np.asarray(samples_ms) * 1e3
+    return dict(mean_us=float(a.mean()), median_us=float(np.median(a)),
+                p10_us=float(np.percentile(a, 10)), p90_us=float(np.percentile(a, 90)))
+
+
+def timed_launches(torch, fn, count):
+    """Run fn(i) count times, each bracketed by events on the current stream.
+    Returns per-launch durations in ms."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
+    torch.cuda.synchronize()
+    for i in range(count):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def rotation_copies(torch, R, layout, n, k, base_w, dev, seed0):
+    import synth
+
+    rb = synth.row_bytes(layout, k)
+    count = max(2, -(-ROTATE_MIN_BYTES // (n * rb)))
+    copies = [torch.from_numpy(base_w).to(dev)]
+    for i in range(1, count):
+        copies.append(synth.weights_device(layout, n, k, seed0 + i, dev))
+    return copies
+
+
+def bench_gemv_graph(torch, R, copies, layout, n, k, x, y, steps, warmup):
+    """Headline: K GEMV launches captured in one graph, replayed in the timed region."""
+    nc = len(copies)
+    for i in range(warmup):
+        R.rfp4_gemv(copies[i % nc], layout, n, k, x, y)
+    torch.cuda.synchronize()
+    eager_ref = R.rfp4_gemv(copies[(steps - 1) % nc], layout, n, k, x).clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        R.rfp4_gemv(copies[0], layout, n, k, x, y)  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            R.rfp4_gemv(copies[i % nc], layout, n, k, x, y)
+    g.replay()  # untimed replay, checked below against the eager result
+    torch.cuda.synchronize()
+    replay_ok = bool(torch.equal(y, eager_ref))
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    replay_ok = replay_ok and bool(torch.equal(y, eager_ref))
+    return (t1 - t0) * 1e3, replay_ok
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--pmc-mode", action="store_true",
+                    help="for rocprofv3 --pmc: a few headline GEMV launches and one plain "
+                         "512 MiB device copy (the byte-count calibration), then exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the ROCmFP4 "
+                          "contraction is measured per GPU; multi-GPU sharding is not built"}))
+        sys.exit(2)
+
+    import torch
+
+    import gemm_rfp4_block_amd as R
+    import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    R.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} CUs={props.multi_processor_count} lib={R.library_path()}")
+
+    # ---------------- headline: up-projection GEMV, dual, fp16, batch 1
+    w_host, x_host, cfg = synth.gemv_inputs("up")
+    n, k, layout = cfg["n"], cfg["k"], cfg["layout"]
+    copies = rotation_copies(torch, R, layout, n, k, w_host, dev, 100)
+    x = x_host.to(dev)
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+    w_bytes = n * synth.row_bytes(layout, k)
+    alg_bytes = w_bytes + k * 2 + n * 4
+    log(f"gemv up: {len(copies)} rotation copies ({len(copies) * w_bytes / 2**20:.0f} MiB)")
+
+    if args.pmc_mode:
+        nc = len(copies)
+        for i in range(max(args.steps, 24)):
+            R.rfp4_gemv(copies[i % nc], layout, n, k, x, y)
+        src = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"pmc mode done: {max(args.steps, 24)} gemv launches of {alg_bytes} algorithmic bytes, "
+            f"one copy of {src.numel()} bytes")
+        return
+
+    graph_ms, replay_ok = bench_gemv_graph(torch, R, copies, layout, n, k, x, y, args.steps, args.warmup)
+    ms_per_step = graph_ms / args.steps
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+
+    nc = len(copies)
+    durs = timed_launches(torch, lambda i: R.rfp4_gemv(copies[i % nc], layout, n, k, x, y), args.steps)
+    st = stats_us(durs)
+    achieved = alg_bytes / (st["mean_us"] * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash(GEMV_SOURCES):
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_kernel<dual,f16,batch1,x in LDS>",
+                "per_launch_bytes": alg_bytes, "launch_us": st}
+    log(f"gemv up: graph {ms_per_step * 1e3:.2f} us/step -> {value:.0f} GB/s; "
+        f"events mean {st['mean_us']:.2f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
+
+    extra = {"gemv_up_graph_replay_matches_eager": replay_ok}
+    del copies
+    torch.cuda.empty_cache()
+
+    # ---------------- down-projection GEMV, fast layout, bf16, batch 1/2/4/8 (1% stress blocks)
+    wd_host, xd_host, dcfg = synth.gemv_inputs("down")
+    dn, dk, dl = dcfg["n"], dcfg["k"], dcfg["layout"]
+    dcopies = rotation_copies(torch, R, dl, dn, dk, wd_host, dev, 200)
+    dw_bytes = dn * synth.row_bytes(dl, dk)
+    down = {}
+    for b in (1, 2, 4, 8):
+        xb = xd_host[:b].contiguous().to(dev)
+        yb = torch.empty((b, dn), dtype=torch.float32, device=dev)
+        for i in range(10):
+            R.rfp4_gemv(dcopies[i % len(dcopies)], dl, dn, dk, xb, yb)
+        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemv(dcopies[i % len(dcopies)], dl, dn, dk, xb, yb), 100))
+        bts = dw_bytes + b * dk * 2 + b * dn * 4
+        down[f"b{b}"] = {"GB/s": round(bts / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": bts, **{kk: round(v, 2) for kk, v in d.items()}}
+        log(f"gemv down b={b}: mean {d['mean_us']:.2f} us -> {down[f'b{b}']['GB/s']:.0f} GB/s")
+    extra["gemv_down_fast_bf16"] = down
+    del dcopies
+    torch.cuda.empty_cache()
+
+    # ---------------- dequant (write-bound)
+    out = torch.empty((n, k), dtype=torch.float32, device=dev)
+    wq = torch.from_numpy(w_host).to(dev)
+    for _ in range(3):
+        R.rfp4_dequant(wq, layout, n, k, out)
+    d = stats_us(timed_launches(torch, lambda i: R.rfp4_dequant(wq, layout, n, k, out), 20))
+    dq_bytes = w_bytes + n * k * 4
+    extra["dequant_up"] = {"GB/s": round(dq_bytes / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": dq_bytes,
+                           "mean_us": round(d["mean_us"], 2)}
+    log(f"dequant: {d['mean_us']:.1f} us -> {extra['dequant_up']['GB/s']:.0f} GB/s")
+    del out
+    torch.cuda.empty_cache()
+
+    # ---------------- prefill GEMM
+    gemm = None
+    if not args.no_gemm:
+        wg_host, a_host, gcfg = synth.gemm_inputs("prefill")
+        gn, gk, gm = gcfg["n"], gcfg["k"], gcfg["m"]
+        wg = torch.from_numpy(wg_host).to(dev)
+        a = a_host.to(dev)
+        c = torch.empty((gm, gn), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c)
+        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c), 20))
+        flops = 2.0 * gm * gn * gk
+        tf = flops / (d["mean_us"] * 1e-6) / 1e12
+        gemm = {"TFLOP/s": round(tf, 1), "flop": flops, "m": gm, "n": gn, "k": gk,
+                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                **{kk: round(v, 2) for kk, v in d.items()}}
+        log(f"gemm: mean {d['mean_us']:.1f} us -> {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
+        del wg, a, c
+        torch.cuda.empty_cache()
+
+    # ---------------- 64-layer decode sweep (448 dual GEMVs, fresh fp16 x per GEMV)
+    if not args.no_sweep:
+        mats, xs, ys, total = [], [], [], 0
+        for layer in range(synth.SWEEP_LAYERS):
+            for pi, (name, sn, sk) in enumerate(synth.SWEEP_SHAPES):
+                seed = 10_000 + layer * 16 + pi
+                mats.append((synth.weights_device(0, sn, sk, seed, dev), sn, sk))
+                xs.append(synth.activations_device(1, sk, "f16", seed, dev))
+                ys.append(torch.empty((1, sn), dtype=torch.float32, device=dev))
+                total += sn * synth.row_bytes(0, sk) + sk * 2 + sn * 4
+        torch.cuda.synchronize()
+
+        def sweep():
+            for (wm, sn, sk), xx, yy in zip(mats, xs, ys):
+                R.rfp4_gemv(wm, 0, sn, sk, xx, yy)
+
+        sweep()
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            sweep()
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            sweep()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        sweep_ms = (time.perf_counter() - t0) * 1e3 / reps
+        extra["sweep_64_layers"] = {"GB/s": round(total / (sweep_ms * 1e-3) / 1e9, 1), "bytes": total,
+                                    "ms_per_sweep": round(sweep_ms, 3), "launches": len(mats),
+                                    "tokens_per_s_equivalent": round(1e3 / sweep_ms, 1)}
+        log(f"sweep: {sweep_ms:.3f} ms -> {extra['sweep_64_layers']['GB/s']:.0f} GB/s")
+        del mats, xs, ys
+        torch.cuda.empty_cache()
+
+    # ---------------- CPU baseline: the fp64 oracle on the host
+    cpu = None
+    if not args.no_cpu:
+        import oracle.rfp4_oracle as O
+
+        try:
+            from threadpoolctl import threadpool_info
+
+            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = 1
+        xh = x_host.double().numpy()
+        reps, t_cpu = 0, 0.0
+        while t_cpu < 10.0 and reps < 8:
+            t0 = time.perf_counter()
+            O.gemv(w_host, layout, n, k, xh)
+            t_cpu += time.perf_counter() - t0
+            reps += 1
+        cpu = {"value": round(alg_bytes * reps / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+               "kind": "oracle",
+               "sample": f"{reps} full up-projection GEMVs (dequant + fp64 matvec + |w||x| denominator), "
+                         f"{t_cpu:.1f} s; host has {len(os.sched_getaffinity(0))} usable cores"}
+        log(f"cpu oracle: {cpu['value']} GB/s over {reps} reps")
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded ROCmFP4 bytes: uniform indices, E4M3 scale exponents 4..9; fp16 x ~ N(0,1))",
+        "config": {"workload": "ROCmFP4 dual-scale up-projection GEMV, weight 17408 x 5120, fp16 x, batch 1, fp32 y",
+                   "rotation_copies": nc, "timing": "HIP graph of K launches, wall clock"},
+        "roofline": roofline, "cpu_baseline": cpu, "gemm": gemm, "extra": extra,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

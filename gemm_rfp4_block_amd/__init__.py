@@ -1,0 +1,172 @@
+"""Python binding of librfp4.so (ROCmFP4 decode, GEMV and GEMM on MI355X).
+
+Argument marshalling only: each function passes tensor data pointers, sizes and the
+current HIP stream to the C entry point of the same name (include/rfp4.h) and raises
+on a non-zero status. Every step of the computation runs in the HIP kernels; there
+is no CPU fallback. If librfp4.so has not been built, the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librfp4.so")
+
+RFP4_DUAL = 0
+RFP4_FAST = 1
+RFP4_F16 = 0
+RFP4_BF16 = 1
+
+RFP4_OK = 0
+RFP4_ERR_NULL = 1
+RFP4_ERR_SHAPE = 2
+RFP4_ERR_UNSUPPORTED = 3
+RFP4_ERR_NONFINITE_SCALE = 4
+RFP4_ERR_HIP = 5
+
+EXPORTED = ("rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
+            "rfp4_dequant", "rfp4_gemv", "rfp4_gemm")
+
+
+class Rfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({rfp4_status_string(status)})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load librfp4.so once; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m gemm_rfp4_block_amd.build` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    L = ctypes.CDLL(_LIB_PATH)
+    c_i64, c_int, c_vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    L.rfp4_block_bytes.argtypes = [c_int]
+    L.rfp4_block_bytes.restype = ctypes.c_size_t
+    L.rfp4_row_bytes.argtypes = [c_int, c_i64]
+    L.rfp4_row_bytes.restype = c_i64
+    L.rfp4_status_string.argtypes = [c_int]
+    L.rfp4_status_string.restype = ctypes.c_char_p
+    L.rfp4_validate.argtypes = [c_vp, c_int, c_i64, c_i64, ctypes.POINTER(c_i64)]
+    L.rfp4_validate.restype = c_int
+    L.rfp4_dequant.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_vp]
+    L.rfp4_dequant.restype = c_int
+    L.rfp4_gemv.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_vp]
+    L.rfp4_gemv.restype = c_int
+    L.rfp4_gemm.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]
+    L.rfp4_gemm.restype = c_int
+    _lib = L
+    return L
+
+
+def rfp4_block_bytes(layout: int) -> int:
+    return int(lib().rfp4_block_bytes(layout))
+
+
+def rfp4_row_bytes(layout: int, k: int) -> int:
+    return int(lib().rfp4_row_bytes(layout, k))
+
+
+def rfp4_status_string(status: int) -> str:
+    return lib().rfp4_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != RFP4_OK:
+        raise Rfp4Error(status, where)
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _xdtype(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return RFP4_F16
+    if t.dtype == torch.bfloat16:
+        return RFP4_BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+
+
+def rfp4_validate(w_host, layout: int, n: int, k: int):
+    """Host-side row validation. ``w_host``: CPU uint8 numpy array or torch tensor,
+    contiguous. Returns (status, first_bad_block)."""
+    import numpy as np
+
+    if hasattr(w_host, "numpy"):
+        w_host = w_host.numpy()
+    arr = np.ascontiguousarray(w_host, dtype=np.uint8)
+    bad = ctypes.c_int64(-1)
+    st = lib().rfp4_validate(arr.ctypes.data_as(ctypes.c_void_p), layout, n, k, ctypes.byref(bad))
+    return int(st), int(bad.value)
+
+
+def rfp4_dequant(w, layout: int, n: int, k: int, out=None, ldo: int | None = None, stream=None):
+    """Dequantize device weights ``w`` (uint8, n x row_bytes) into fp32 ``out`` (n x ldo)."""
+    import torch
+
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    if ldo is None:
+        ldo = out.stride(0) if out.dim() == 2 else k
+    _check(lib().rfp4_dequant(_ptr(w), layout, n, k, _ptr(out), ldo, _stream(stream)), "rfp4_dequant")
+    return out
+
+
+def rfp4_gemv(w, layout: int, n: int, k: int, x, y=None, stream=None):
+    """y[b, r] = sum_c W[r, c] x[b, c]; ``x`` (batch, k) f16/bf16 on the device, y fp32."""
+    import torch
+
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    batch = x.shape[0]
+    if y is None:
+        y = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    ldx = x.stride(0) if batch > 1 else max(k, x.stride(0))
+    ldy = y.stride(0) if y.dim() == 2 and batch > 1 else max(n, y.stride(0) if y.dim() == 2 else n)
+    _check(lib().rfp4_gemv(_ptr(w), layout, n, k, _ptr(x), _xdtype(x), batch, ldx, _ptr(y), ldy,
+                           _stream(stream)), "rfp4_gemv")
+    return y
+
+
+def rfp4_gemm(w, layout: int, n: int, k: int, a, c=None, stream=None):
+    """C = A W^T with A (m, k) bf16 and C (m, n) bf16 on the device."""
+    import torch
+
+    m = a.shape[0]
+    if c is None:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    _check(lib().rfp4_gemm(_ptr(w), layout, n, k, _ptr(a), m, a.stride(0), _ptr(c), c.stride(0),
+                           _stream(stream)), "rfp4_gemm")
+    return c
+
+
+__all__ = [
+    "RFP4_DUAL", "RFP4_FAST", "RFP4_F16", "RFP4_BF16", "Rfp4Error", "lib", "library_path",
+    "rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
+    "rfp4_dequant", "rfp4_gemv", "rfp4_gemm",
+]

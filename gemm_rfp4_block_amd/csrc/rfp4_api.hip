@@ -1,0 +1,121 @@
+// Host side of librfp4.so: the C ABI declared in include/rfp4.h.
+//
+// Every argument is checked here, before any HIP call, so that argument errors are
+// reported on machines without a GPU and never reach a kernel. The row validation of
+// "Feasibility Report: Porting ROCmFP4 to Atlas", "Scale Format" (reject non-finite
+// scale bytes at load time) runs on the host in rfp4_validate.
+
+#include "rfp4.h"
+
+#include <stdint.h>
+
+#include "rfp4_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 2147483647;  // n, m, k <= 2^31 - 1
+
+bool layout_ok(int layout) { return layout == RFP4_DUAL || layout == RFP4_FAST; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape and alignment of the packed weight matrix, shared by every device entry point.
+rfp4_status check_weights(const void* w, int layout, int64_t n, int64_t k) {
+  if (!layout_ok(layout)) return RFP4_ERR_UNSUPPORTED;
+  if (n < 1 || n > kMaxDim || k < 32 || k > kMaxDim || (k % 32) != 0) return RFP4_ERR_SHAPE;
+  if (w == nullptr) return RFP4_ERR_NULL;
+  const int64_t row = (k / 32) * rfp4::block_bytes(layout);
+  if (!aligned16(w) || (row % 16) != 0) return RFP4_ERR_UNSUPPORTED;
+  return RFP4_OK;
+}
+
+rfp4_status from_hip(hipError_t e) { return e == hipSuccess ? RFP4_OK : RFP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t rfp4_block_bytes(int layout) {
+  return layout_ok(layout) ? static_cast<size_t>(rfp4::block_bytes(layout)) : 0;
+}
+
+int64_t rfp4_row_bytes(int layout, int64_t k) {
+  if (!layout_ok(layout) || k < 32 || k > kMaxDim || (k % 32) != 0) return -1;
+  return (k / 32) * rfp4::block_bytes(layout);
+}
+
+const char* rfp4_status_string(int status) {
+  switch (status) {
+    case RFP4_OK: return "ok";
+    case RFP4_ERR_NULL: return "a required pointer is NULL";
+    case RFP4_ERR_SHAPE: return "shape out of range (n, m, k, batch or a leading dimension)";
+    case RFP4_ERR_UNSUPPORTED: return "unsupported layout, dtype or alignment";
+    case RFP4_ERR_NONFINITE_SCALE: return "non-finite scale byte (low seven bits all ones)";
+    case RFP4_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+rfp4_status rfp4_validate(const uint8_t* w_host, int layout, int64_t n, int64_t k,
+                          int64_t* first_bad_block) {
+  if (first_bad_block) *first_bad_block = -1;
+  if (!layout_ok(layout)) return RFP4_ERR_UNSUPPORTED;
+  if (n < 1 || n > kMaxDim || k < 32 || k > kMaxDim || (k % 32) != 0) return RFP4_ERR_SHAPE;
+  if (w_host == nullptr) return RFP4_ERR_NULL;
+  const int bb = rfp4::block_bytes(layout);
+  const int nscale = bb - 16;
+  const int64_t blocks = n * (k / 32);
+  const uint8_t* p = w_host + 16;  // first scale byte of block 0
+  for (int64_t b = 0; b < blocks; ++b, p += bb) {
+    for (int s = 0; s < nscale; ++s) {
+      if ((p[s] & 0x7F) == 0x7F) {
+        if (first_bad_block) *first_bad_block = b;
+        return RFP4_ERR_NONFINITE_SCALE;
+      }
+    }
+  }
+  return RFP4_OK;
+}
+
+rfp4_status rfp4_dequant(const void* w, int layout, int64_t n, int64_t k, float* out,
+                         int64_t ldo, void* stream) {
+  rfp4_status st = check_weights(w, layout, n, k);
+  if (st != RFP4_OK) return st;
+  if (ldo < k || ldo > (int64_t(1) << 40) / n) return RFP4_ERR_SHAPE;
+  if (out == nullptr) return RFP4_ERR_NULL;
+  if (!aligned16(out) || (ldo % 4) != 0) return RFP4_ERR_UNSUPPORTED;
+  return from_hip(rfp4::launch_dequant(static_cast<const uint8_t*>(w), layout, n, k, out, ldo,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const void* x,
+                      int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,
+                      void* stream) {
+  rfp4_status st = check_weights(w, layout, n, k);
+  if (st != RFP4_OK) return st;
+  if (xdtype != RFP4_F16 && xdtype != RFP4_BF16) return RFP4_ERR_UNSUPPORTED;
+  if (batch < 1 || batch > 8) return RFP4_ERR_SHAPE;
+  if (ldx < k || ldy < n || ldx > kMaxDim || ldy > kMaxDim) return RFP4_ERR_SHAPE;
+  if (x == nullptr || y == nullptr) return RFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || (ldx % 8) != 0) return RFP4_ERR_UNSUPPORTED;
+  return from_hip(rfp4::launch_gemv(static_cast<const uint8_t*>(w), layout, n, k, x, xdtype,
+                                    static_cast<int>(batch), ldx, y, ldy,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
+                      int64_t m, int64_t lda, void* c, int64_t ldc, void* stream) {
+  rfp4_status st = check_weights(w, layout, n, k);
+  if (st != RFP4_OK) return st;
+  if (m < 1 || m > kMaxDim) return RFP4_ERR_SHAPE;
+  if (lda < k || ldc < n || lda > kMaxDim || ldc > kMaxDim) return RFP4_ERR_SHAPE;
+  if (a == nullptr || c == nullptr) return RFP4_ERR_NULL;
+  if (!aligned16(a) || !aligned16(c) || (lda % 8) != 0 || (ldc % 8) != 0)
+    return RFP4_ERR_UNSUPPORTED;
+  return from_hip(rfp4::launch_gemm(static_cast<const uint8_t*>(w), layout, n, k,
+                                    static_cast<const uint16_t*>(a), m, lda,
+                                    static_cast<uint16_t*>(c), ldc,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Internal declarations shared by the host API and the kernel translation units of
+// librfp4.so. Not part of the public ABI (see include/rfp4.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rfp4 {
+
+constexpr int kDual = 0;
+constexpr int kFast = 1;
+constexpr int kF16 = 0;
+constexpr int kBF16 = 1;
+
+// Bytes per 32-weight block ("Block Layout": qs[16] then e[2] or e).
+constexpr int block_bytes(int layout) { return layout == kDual ? 18 : 17; }
+
+// Launchers. Arguments have been checked by the API layer: shapes in range, rows
+// 16-byte aligned, pointers non-null and aligned as the public header requires.
+hipError_t launch_dequant(const uint8_t* w, int layout, int64_t n, int64_t k, float* out,
+                          int64_t ldo, hipStream_t stream);
+
+hipError_t launch_gemv(const uint8_t* w, int layout, int64_t n, int64_t k, const void* x,
+                       int xdtype, int batch, int64_t ldx, float* y, int64_t ldy,
+                       hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
+                       int64_t m, int64_t lda, uint16_t* c, int64_t ldc, hipStream_t stream);
+
+}  // namespace rfp4

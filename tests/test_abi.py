@@ -1,0 +1,157 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load on a machine without a GPU, export every function that
+include/rfp4.h declares, and reject bad arguments before making any HIP call (so
+every call below carries at least one invalid argument and never launches a kernel).
+Host-side row validation is compared with the oracle's.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import gemm_rfp4_block_amd as R
+import oracle.rfp4_oracle as O
+import synth
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "rfp4.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(R.library_path()):
+        from gemm_rfp4_block_amd.build import build
+
+        build()
+    return R.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"RFP4_API\s+[\w\s\*]+?\b(rfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(R.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True)
+    exported = set(re.findall(r" T (rfp4_\w+)", out.stdout))
+    assert exported == set(declared_functions())
+
+
+def test_block_and_row_bytes(L):
+    assert R.rfp4_block_bytes(R.RFP4_DUAL) == O.block_bytes(O.DUAL) == 18
+    assert R.rfp4_block_bytes(R.RFP4_FAST) == O.block_bytes(O.FAST) == 17
+    assert R.rfp4_block_bytes(7) == 0
+    for k in (32, 512, 5120, 17408):
+        assert R.rfp4_row_bytes(R.RFP4_DUAL, k) == O.row_bytes(O.DUAL, k)
+        assert R.rfp4_row_bytes(R.RFP4_FAST, k) == O.row_bytes(O.FAST, k)
+    assert R.rfp4_row_bytes(R.RFP4_DUAL, 33) == -1
+    assert R.rfp4_row_bytes(R.RFP4_DUAL, 0) == -1
+    assert R.rfp4_row_bytes(5, 64) == -1
+
+
+def test_status_strings(L):
+    for st in range(6):
+        assert R.rfp4_status_string(st)
+    assert R.rfp4_status_string(99) == "unknown status"
+
+
+# Fake, 16-byte aligned "device" addresses. Every call below fails an argument check
+# first, so these are never dereferenced or handed to HIP.
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+NULL = ctypes.c_void_p(0)
+UNALIGNED = ctypes.c_void_p(0x10008)
+
+
+def test_dequant_argument_errors(L):
+    f = L.rfp4_dequant
+    assert f(NULL, 0, 4, 512, P2, 512, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 4, 512, NULL, 512, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 2, 4, 512, P2, 512, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 0, 0, 512, P2, 512, NULL) == R.RFP4_ERR_SHAPE
+    assert f(P, 0, 4, 500, P2, 512, NULL) == R.RFP4_ERR_SHAPE
+    assert f(P, 0, 4, 0, P2, 512, NULL) == R.RFP4_ERR_SHAPE
+    assert f(P, 0, 4, 512, P2, 511, NULL) == R.RFP4_ERR_SHAPE  # ldo < k
+    assert f(P, 0, 4, 96, P2, 96, NULL) == R.RFP4_ERR_UNSUPPORTED  # dual row not 16-B multiple
+    assert f(P, 1, 4, 256, P2, 256, NULL) == R.RFP4_ERR_UNSUPPORTED  # fast needs k % 512
+    assert f(UNALIGNED, 0, 4, 512, P2, 512, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 0, 4, 512, UNALIGNED, 512, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 0, 4, 512, P2, 514, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldo % 4
+
+
+def test_gemv_argument_errors(L):
+    f = L.rfp4_gemv
+    assert f(NULL, 0, 8, 512, P2, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 8, 512, NULL, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 8, 512, P2, 0, 1, 512, NULL, 8, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 8, 512, P2, 2, 1, 512, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # dtype
+    assert f(P, 3, 8, 512, P2, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # layout
+    assert f(P, 0, 8, 512, P2, 0, 0, 512, P, 8, NULL) == R.RFP4_ERR_SHAPE  # batch 0
+    assert f(P, 0, 8, 512, P2, 0, 9, 512, P, 8, NULL) == R.RFP4_ERR_SHAPE  # batch 9
+    assert f(P, 0, 8, 512, P2, 0, 1, 500, P, 8, NULL) == R.RFP4_ERR_SHAPE  # ldx < k
+    assert f(P, 0, 8, 512, P2, 0, 1, 512, P, 7, NULL) == R.RFP4_ERR_SHAPE  # ldy < n
+    assert f(P, 0, -1, 512, P2, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_SHAPE
+    assert f(P, 0, 8, 2**31, P2, 0, 1, 2**31, P, 8, NULL) == R.RFP4_ERR_SHAPE
+    assert f(P, 0, 8, 512, P2, 0, 2, 516, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldx % 8
+    assert f(P, 0, 8, 512, UNALIGNED, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 0, 8, 512, P2, 0, 1, 512, UNALIGNED, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 1, 8, 768, P2, 0, 1, 768, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # fast k % 512
+
+
+def test_gemm_argument_errors(L):
+    f = L.rfp4_gemm
+    assert f(NULL, 0, 64, 512, P2, 16, 512, P, 64, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 64, 512, NULL, 16, 512, P, 64, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 64, 512, P2, 16, 512, NULL, 64, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 64, 512, P2, 0, 512, P, 64, NULL) == R.RFP4_ERR_SHAPE  # m = 0
+    assert f(P, 0, 64, 512, P2, 16, 511, P, 64, NULL) == R.RFP4_ERR_SHAPE  # lda < k
+    assert f(P, 0, 64, 512, P2, 16, 512, P, 63, NULL) == R.RFP4_ERR_SHAPE  # ldc < n
+    assert f(P, 0, 64, 512, P2, 16, 520, P, 68, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldc % 8
+    assert f(P, 0, 64, 512, P2, 16, 516, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED  # lda % 8
+    assert f(P, 4, 64, 512, P2, 16, 512, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 0, 64, 96, P2, 16, 96, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED
+
+
+def test_validate_null_and_shape(L):
+    bad = ctypes.c_int64(123)
+    assert L.rfp4_validate(NULL, 0, 1, 32, ctypes.byref(bad)) == R.RFP4_ERR_NULL
+    assert bad.value == -1
+    buf = (ctypes.c_uint8 * 18)()
+    assert L.rfp4_validate(buf, 0, 1, 31, None) == R.RFP4_ERR_SHAPE
+    assert L.rfp4_validate(buf, 9, 1, 32, None) == R.RFP4_ERR_UNSUPPORTED
+    assert L.rfp4_validate(buf, 0, 1, 32, None) == R.RFP4_OK
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_validate_matches_oracle(L, layout):
+    rng = np.random.default_rng(11 + layout)
+    n, k = 24, 1024
+    w = synth.weights(rng, layout, n, k)
+    assert R.rfp4_validate(w, layout, n, k) == (R.RFP4_OK, -1)
+    assert O.validate(w, layout, n, k) == (True, -1)
+    bb = synth.block_bytes(layout)
+    nb = k // 32
+    for trial in range(20):
+        wb = w.reshape(n, nb, bb).copy()
+        cnt = int(rng.integers(1, 4))
+        for _ in range(cnt):
+            r, j = int(rng.integers(0, n)), int(rng.integers(0, nb))
+            s = int(rng.integers(16, bb))
+            wb[r, j, s] = 0x7F | (int(rng.integers(0, 2)) << 7)
+        wb[:, :, :16] |= 0x7F  # index bytes never count
+        flat = wb.reshape(n, -1)
+        ok, first = O.validate(flat, layout, n, k)
+        st, bad = R.rfp4_validate(flat, layout, n, k)
+        assert not ok
+        assert st == R.RFP4_ERR_NONFINITE_SCALE and bad == first

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Acceptance: dequantization bit-exact (uint32 views, signs of zero included); GEMV and
+GEMM max |y - y_ref| / sum |w x| <= 2e-3 (outputs with a zero denominator must be
+exactly zero). Inputs come from the seeded generators in synth/. Full-size workloads
+run in the launch configuration the benchmark times; the GEMM at full size is checked
+on a seeded sample of output columns that the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_rfp4_block_amd as R
+import oracle.rfp4_oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def x64(t):
+    return t.to(torch.float64).cpu().numpy()
+
+
+def bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def run_gemv(w, layout, n, k, x, ldx=None, ldy=None):
+    """Call rfp4_gemv with optional padded leading dimensions; returns (batch, n) fp32."""
+    batch = x.shape[0]
+    if ldx is None or ldx == k:
+        xd = x.to(DEV).contiguous()
+        ldx = k
+    else:
+        buf = torch.zeros((batch, ldx), dtype=x.dtype, device=DEV)
+        buf[:, :k] = x.to(DEV)
+        xd = buf
+    ldy = n if ldy is None else ldy
+    y = torch.full((batch, ldy), float("nan"), dtype=torch.float32, device=DEV)
+    wd = dev(w)
+    st = R.lib().rfp4_gemv(R._ptr(wd), layout, n, k, R._ptr(xd), R._xdtype(xd), batch, ldx,
+                           R._ptr(y), ldy, R._stream(None))
+    assert st == R.RFP4_OK, R.rfp4_status_string(st)
+    torch.cuda.synchronize()
+    out = y.cpu().numpy()
+    if ldy > n:
+        assert np.all(np.isnan(out[:, n:])), "gemv wrote past n"
+    return out[:, :n]
+
+
+# ------------------------------------------------------------------ dequant
+
+def test_dequant_tiny_bitwise():
+    w, _, cfg = synth.gemv_inputs("tiny")
+    n, k = cfg["n"], cfg["k"]
+    got = R.rfp4_dequant(dev(w), cfg["layout"], n, k).cpu().numpy()
+    assert np.array_equal(bits(got), bits(O.dequantize_f32(w, cfg["layout"], n, k)))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_dequant_every_scale_byte_and_index(layout):
+    """256 rows: row b uses scale byte b (dual: second half (b*37+11) % 256) on blocks
+    that hold every one of the 16 indices in both nibble positions."""
+    k = 512
+    nb = k // 32
+    qs = np.array([t | ((15 - t) << 4) for t in range(16)], dtype=np.uint8)
+    rows = []
+    for b in range(256):
+        blk = []
+        for j in range(nb):
+            q = np.roll(qs, j)
+            if layout == 0:
+                blk.append(np.concatenate([q, [b, (b * 37 + 11) % 256]]).astype(np.uint8))
+            else:
+                blk.append(np.concatenate([q, [b]]).astype(np.uint8))
+        rows.append(np.concatenate(blk))
+    w = np.stack(rows)
+    got = R.rfp4_dequant(dev(w), layout, 256, k).cpu().numpy()
+    exp = O.dequantize_f32(w, layout, 256, k)
+    assert np.array_equal(bits(got), bits(exp))
+
+
+@pytest.mark.parametrize("name", ["up", "down"])
+def test_dequant_full_size_bitwise(name):
+    w, _, cfg = synth.gemv_inputs(name)
+    n, k = cfg["n"], cfg["k"]
+    got = R.rfp4_dequant(dev(w), cfg["layout"], n, k).cpu().numpy()
+    exp = O.dequantize_f32(w, cfg["layout"], n, k)
+    assert np.array_equal(bits(got), bits(exp))
+
+
+def test_dequant_padded_ldo():
+    rng = np.random.default_rng(21)
+    n, k, ldo = 19, 512, 532
+    w = synth.weights(rng, 1, n, k)
+    out = torch.full((n, ldo), -7.0, dtype=torch.float32, device=DEV)
+    R.rfp4_dequant(dev(w), 1, n, k, out=out, ldo=ldo)
+    o = out.cpu().numpy()
+    assert np.array_equal(bits(o[:, :k]), bits(O.dequantize_f32(w, 1, n, k)))
+    assert np.all(o[:, k:] == -7.0)
+
+
+# ------------------------------------------------------------------ GEMV
+
+def check_gemv(w, layout, n, k, x, **kw):
+    y = run_gemv(w, layout, n, k, x, **kw)
+    y_ref, den = O.gemv(w, layout, n, k, x64(x))
+    err = O.normalized_error(y, y_ref, den)
+    assert err <= TOL, err
+    return y, err
+
+
+def test_gemv_tiny():
+    w, x, cfg = synth.gemv_inputs("tiny")
+    check_gemv(w, cfg["layout"], cfg["n"], cfg["k"], x)
+
+
+def test_gemv_up_full():
+    w, x, cfg = synth.gemv_inputs("up")
+    check_gemv(w, cfg["layout"], cfg["n"], cfg["k"], x)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_gemv_down_full_stress(batch):
+    w, x, cfg = synth.gemv_inputs("down", batch=batch)
+    check_gemv(w, cfg["layout"], cfg["n"], cfg["k"], x)
+
+
+RAGGED = [  # layout, n, k, batch, dtype, ldx, ldy
+    (0, 1, 256, 1, "f16", None, None),
+    (0, 3, 768, 2, "bf16", 776, 9),
+    (0, 37, 2304, 3, "f16", None, 40),
+    (0, 130, 256, 8, "bf16", 264, None),
+    (0, 257, 4096, 5, "f16", None, None),
+    (1, 1, 512, 1, "bf16", None, None),
+    (1, 45, 1536, 6, "f16", 1544, 48),
+    (1, 67, 512, 7, "bf16", None, None),
+    (1, 300, 8192, 8, "f16", None, None),
+    (0, 1000, 6144, 1, "bf16", None, None),
+    (1, 513, 17408, 1, "f16", None, None),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "L{}n{}k{}b{}{}".format(*c[:5]))
+def test_gemv_ragged(case):
+    layout, n, k, batch, dt, ldx, ldy = case
+    rng = np.random.default_rng(1000 + n + k + batch)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    x = synth.activations(rng, batch, k, dt)
+    check_gemv(w, layout, n, k, x, ldx=ldx, ldy=ldy)
+
+
+def test_gemv_zero_scales_give_zero():
+    rng = np.random.default_rng(31)
+    n, k = 64, 1024
+    w = synth.weights(rng, 0, n, k).reshape(n, k // 32, 18)
+    w[:, :, 16:] = np.where(rng.integers(0, 2, size=w[:, :, 16:].shape) == 1, 0x80, 0x00)
+    x = synth.activations(rng, 3, k, "f16")
+    y = run_gemv(w.reshape(n, -1), 0, n, k, x)
+    assert np.all(y == 0.0)
+
+
+def test_gemv_one_hot_selects_a_column():
+    rng = np.random.default_rng(32)
+    n, k = 96, 2048
+    w = synth.weights(rng, 0, n, k)
+    wd = O.dequantize_f32(w, 0, n, k)
+    for j in (0, 31, 32, 1000, 2047):
+        x = torch.zeros((1, k), dtype=torch.float16)
+        x[0, j] = 1.0
+        y = run_gemv(w, 0, n, k, x)
+        assert np.array_equal(y[0], wd[:, j])  # numeric equality: one exact product
+
+
+def test_gemv_extreme_values():
+    """Largest finite scales, all-magnitude-10 codes and the largest fp16 activations:
+    the fp32 accumulation must neither overflow nor lose the result."""
+    n, k = 16, 4096
+    rng = np.random.default_rng(33)
+    w = synth.weights(rng, 0, n, k).reshape(n, k // 32, 18)
+    w[:, :, :16] = np.where(rng.integers(0, 2, size=(n, k // 32, 16)) == 1, 0xF7, 0x7F)
+    w[:, :, 16:] = 0x7E
+    x = torch.full((2, k), 65504.0, dtype=torch.float16)
+    x[1, ::2] = -65504.0
+    check_gemv(w.reshape(n, -1), 0, n, k, x)
+
+
+@pytest.mark.parametrize("layout,dt", [(0, "f16"), (1, "bf16")])
+def test_gemv_exact_invariants(layout, dt):
+    """Toggling every index sign negates y bitwise; +1 on every scale exponent field
+    doubles y bitwise; two runs agree bitwise."""
+    rng = np.random.default_rng(34 + layout)
+    n, k = 200, 4096
+    w = synth.weights(rng, layout, n, k)
+    x = synth.activations(rng, 4, k, dt)
+    bb = synth.block_bytes(layout)
+    y = run_gemv(w, layout, n, k, x)
+    y_again = run_gemv(w, layout, n, k, x)
+    assert np.array_equal(bits(y), bits(y_again))
+    blocks = w.reshape(n, k // 32, bb)
+    flip = blocks.copy()
+    flip[:, :, :16] ^= 0x88
+    yf = run_gemv(flip.reshape(n, -1), layout, n, k, x)
+    assert np.array_equal(yf, -y)
+    step = blocks.copy()
+    step[:, :, 16:] += 8
+    ys = run_gemv(step.reshape(n, -1), layout, n, k, x)
+    assert np.array_equal(ys, 2 * y)
+
+
+def test_gemv_dual_equal_halves_matches_fast():
+    rng = np.random.default_rng(36)
+    n, k = 128, 2048
+    wf = synth.weights(rng, 1, n, k).reshape(n, k // 32, 17)
+    wd = np.concatenate([wf, wf[:, :, 16:]], axis=2)
+    x = synth.activations(rng, 2, k, "bf16")
+    yf = run_gemv(wf.reshape(n, -1), 1, n, k, x)
+    yd = run_gemv(wd.reshape(n, -1), 0, n, k, x)
+    assert np.array_equal(bits(yf), bits(yd))
+
+
+# ------------------------------------------------------------------ GEMM
+
+def gemm_error(c, c_ref, den):
+    """Normalized error of a bf16-output GEMM. The output format adds its own rounding
+    (half a bf16 ulp of the exact value, up to 2^-8 relative), which the page does not
+    budget for; that part is allowed on top of the 2e-3 bound, which applies to the rest."""
+    c = np.asarray(c, dtype=np.float64)
+    mag = np.abs(c_ref)
+    half_ulp = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 8), 0.0)
+    excess = np.maximum(np.abs(c - c_ref) - half_ulp, 0.0)
+    return O.normalized_error(c_ref + np.sign(c - c_ref) * excess, c_ref, den)
+
+
+def run_gemm(w, layout, n, k, a, ldc=None):
+    m = a.shape[0]
+    ad = a.to(DEV).contiguous()
+    ldc = n if ldc is None else ldc
+    c = torch.full((m, ldc), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wd = dev(w)
+    st = R.lib().rfp4_gemm(R._ptr(wd), layout, n, k, R._ptr(ad), m, k, R._ptr(c), ldc, R._stream(None))
+    assert st == R.RFP4_OK, R.rfp4_status_string(st)
+    torch.cuda.synchronize()
+    out = c.to(torch.float64).cpu().numpy()
+    if ldc > n:
+        assert np.all(np.isnan(out[:, n:])), "gemm wrote past n"
+    return out[:, :n]
+
+
+GEMM_CASES = [  # layout, m, n, k
+    (0, 1, 1, 256), (0, 100, 200, 512), (1, 77, 129, 1024), (0, 128, 128, 256),
+    (0, 257, 300, 2304), (1, 33, 513, 512), (0, 512, 64, 5120),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: "L{}m{}n{}k{}".format(*c))
+def test_gemm_small(case):
+    layout, m, n, k = case
+    rng = np.random.default_rng(2000 + m + n + k)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    a = synth.activations(rng, m, k, "bf16")
+    ldc = (n + 7) // 8 * 8 + 8  # padded leading dimension, multiple of 8
+    c = run_gemm(w, layout, n, k, a, ldc=ldc)
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c, c_ref, den) <= TOL
+
+
+@pytest.mark.parametrize("case", [(0, 100, 200, 512), (1, 77, 136, 1024), (0, 1, 8, 256), (0, 257, 296, 2304)])
+def test_gemm_ragged_mn(case):
+    layout, m, n, k = case
+    rng = np.random.default_rng(3000 + m + n)
+    w = synth.weights(rng, layout, n, k)
+    a = synth.activations(rng, m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a)
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c, c_ref, den) <= TOL
+
+
+def test_gemm_same_sign_rounding():
+    """All terms positive: the bf16 output must be within one bf16 ulp of the exactly
+    rounded oracle value (the normalized metric alone would be dominated by rounding)."""
+    m, n, k = 64, 64, 1024
+    rng = np.random.default_rng(41)
+    w = synth.weights(rng, 0, n, k).reshape(n, k // 32, 18)
+    w[:, :, :16] &= 0x77  # clear both sign bits: all codes >= 0
+    w = w.reshape(n, -1)
+    a = torch.from_numpy(np.abs(rng.standard_normal((m, k))).astype(np.float32)).to(torch.bfloat16)
+    c = run_gemm(w, 0, n, k, a)
+    c_ref, _ = O.gemm(w, 0, n, k, x64(a))
+    ref_bf = torch.from_numpy(c_ref).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    ulp = np.abs(ref_bf) * 2.0 ** -7
+    assert np.all(np.abs(c - ref_bf) <= ulp + 1e-30)
+
+
+def test_gemm_full_size_sampled():
+    w, a, cfg = synth.gemm_inputs("prefill")
+    n, k, m = cfg["n"], cfg["k"], cfg["m"]
+    c = run_gemm(w, cfg["layout"], n, k, a)
+    rng = np.random.default_rng(99)
+    cols = np.sort(rng.choice(n, size=96, replace=False))
+    c_ref, den = O.gemm_rows(w, cfg["layout"], n, k, x64(a), cols)
+    assert gemm_error(c[:, cols], c_ref, den) <= TOL
+    assert np.all(np.isfinite(c))
