@@ -6,21 +6,29 @@
 // kernel therefore reads every packed block exactly once from HBM and does all the
 // decode in registers.
 //
-// Work mapping. A wavefront covers RL rows x CL column lanes (RL * CL = 64, CL =
-// gcd(64, blocks per row)), so every lane owns the same number of blocks of its row
-// and lanes of one row read adjacent blocks (a run of CL * 18 or CL * 17 contiguous
-// bytes per load instruction). Each lane loads a block's 16 index bytes with one
-// unaligned 16-byte load and its scale byte(s) with one small load, decodes the 32
-// weights to f16/bf16 pairs (see rfp4_decode.h) and multiplies them with the
-// activations with v_dot2_f32_{f16,bf16}: one fp32 partial sum per 16-weight half,
-// then one fp32 FMA with that half's E4M3 scale. The partial sums of the CL lanes of
-// a row are combined with a butterfly of cross-lane shuffles, and the final 1/2 of
-// the half-scale is applied at the store.
+// Loads. A lane owns units of P consecutive blocks (P = 1 or 2). A pair (P = 2) is
+// 36 contiguous bytes (dual) or 34 (fast), fetched with two 16-byte loads and one
+// 4-byte (dual) or 2-byte (fast) load: 1.5 memory instructions per block instead of
+// 2 for single blocks (16 index bytes + a small load for the scale bytes), which
+// measurably raises the achieved bandwidth. The second block of a pair starts at byte
+// 18 (dual) or 17 (fast); its index bytes are realigned with v_alignbyte_b32. The
+// launcher uses pairs unless that leaves too few wavefronts for the shape.
 //
-// Activations: staged once per workgroup into LDS when batch * k * 2 bytes fits the
-// budget, in 16-byte units ordered [batch][chunk of 8 values][block] so that the 64
-// lanes of a wavefront read consecutive 16-byte units (no bank conflicts); otherwise
-// read straight from global memory (they stay cache-resident).
+// Work mapping. A wavefront covers RL rows x CL lanes (RL * CL = 64, CL = gcd(64,
+// units per row)); lane c of a row owns units c, c + CL, c + 2 CL, ... of that row, so
+// each load instruction reads runs of CL * 36 (or 34, 18, 17) contiguous bytes. Every
+// wavefront owns `gpw` consecutive row groups and all wavefronts are resident at
+// once, so the work is evenly split. Each lane keeps three units in flight.
+//
+// Arithmetic. Each block's 32 weights are decoded to f16/bf16 pairs (rfp4_decode.h)
+// and multiplied with the activations with v_dot2_f32_{f16,bf16}: one fp32 partial
+// sum per 16-weight half, then one fp32 FMA with that half's E4M3 scale. The partial
+// sums of the CL lanes of a row are combined with a butterfly of cross-lane shuffles
+// and the 1/2 of the half-scale is applied at the store.
+//
+// Activations are staged once per workgroup into LDS when they fit the budget (layout
+// at xs_index); otherwise they are read from global memory, where they stay
+// cache-resident.
 
 #include "rfp4_decode.h"
 #include "rfp4_internal.h"
@@ -30,6 +38,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kXLdsBudget = 40 * 1024;
+
+// Tuning knob (no effect on results): resident wavefronts per CU the launch is sized for.
+#ifndef RFP4_GEMV_WAVES_PER_CU
+#define RFP4_GEMV_WAVES_PER_CU 24
+#endif
 
 template <int XT>
 struct Act;
@@ -52,135 +65,327 @@ struct Act<kBF16> {
   }
 };
 
-template <int LAYOUT, int XT, int BATCH, bool XLDS>
+// Raw bytes of one unit of P consecutive blocks (see the file comment), as words.
+//   P = 1: d[0..3] = index bytes, d[4] = the scale byte(s) in its low bytes.
+//   P = 2: d[0..7] = bytes 0..31, d[8] = bytes 32..35 (dual) or 32..33 (fast).
+template <int P>
+struct UnitRaw {
+  uint32_t d[P == 1 ? 5 : 9];
+};
+
+template <int LAYOUT, int P>
+__device__ __forceinline__ void load_unit(const uint8_t* p, UnitRaw<P>& u) {
+  const uint4 v0 = load16(p);
+  u.d[0] = v0.x;
+  u.d[1] = v0.y;
+  u.d[2] = v0.z;
+  u.d[3] = v0.w;
+  if constexpr (P == 1) {
+    if constexpr (LAYOUT == kDual) {
+      uint16_t t;
+      __builtin_memcpy(&t, p + 16, 2);
+      u.d[4] = t;
+    } else {
+      u.d[4] = p[16];
+    }
+  } else {
+    const uint4 v1 = load16(p + 16);
+    u.d[4] = v1.x;
+    u.d[5] = v1.y;
+    u.d[6] = v1.z;
+    u.d[7] = v1.w;
+    if constexpr (LAYOUT == kDual) {
+      u.d[8] = load4(p + 32);  // 4-byte aligned: units start at multiples of 36 bytes
+    } else {
+      uint16_t t;
+      __builtin_memcpy(&t, p + 32, 2);
+      u.d[8] = t;
+    }
+  }
+}
+
+// The 16 index bytes of block B of a unit, as four words.
+template <int LAYOUT, int P, int B>
+__device__ __forceinline__ uint4 unit_qs(const UnitRaw<P>& u) {
+  constexpr int off = B * block_bytes(LAYOUT);  // byte offset of the block in the unit
+  constexpr int w0 = off / 4;
+  constexpr int sh = off % 4;
+  if constexpr (sh == 0) {
+    return uint4{u.d[w0], u.d[w0 + 1], u.d[w0 + 2], u.d[w0 + 3]};
+  } else {
+    return uint4{__builtin_amdgcn_alignbyte(u.d[w0 + 1], u.d[w0], sh),
+                 __builtin_amdgcn_alignbyte(u.d[w0 + 2], u.d[w0 + 1], sh),
+                 __builtin_amdgcn_alignbyte(u.d[w0 + 3], u.d[w0 + 2], sh),
+                 __builtin_amdgcn_alignbyte(u.d[w0 + 4], u.d[w0 + 3], sh)};
+  }
+}
+
+// E4M3 values of the scale byte(s) of block B (twice the decoded scales). Bit 7 of a
+// scale byte is not part of the value and is cleared first.
+template <int LAYOUT, int P, int B>
+__device__ __forceinline__ void unit_scales(const UnitRaw<P>& u, float& s0, float& s1) {
+  constexpr int off = (P == 1) ? 0 : B * block_bytes(LAYOUT) + 16;
+  constexpr int wi = (P == 1) ? 4 : off / 4;
+  constexpr int bi = off % 4;
+  const uint32_t word = u.d[wi] & 0x7F7F7F7Fu;
+  s0 = e4m3_hw<bi>(word);
+  if constexpr (LAYOUT == kDual) {
+    static_assert(bi == 0 || bi == 2, "dual scale bytes are 2-byte aligned");
+    s1 = e4m3_hw<bi + 1>(word);
+  } else {
+    s1 = s0;
+  }
+}
+
+// One block: decode 32 weights and accumulate them against every activation row.
+// `xunit(b, cc)` returns the 16-byte activation unit cc (values 8cc..8cc+7 of the
+// block) of activation row b. Each half's dot product is split over two chains.
+template <int XT, int BATCH, typename XUnit>
+__device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, XUnit xunit,
+                                          float (&acc)[BATCH]) {
+  typedef Act<XT> A;
+  typedef typename A::pair pair;
+  const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
+  pair wl[8], wh[8];  // first half (low nibbles), second half (high nibbles)
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t lo = codes_low(q[d]);
+    const uint32_t hi = codes_high(q[d]);
+    wl[2 * d] = A::decode(lo, false);
+    wl[2 * d + 1] = A::decode(lo, true);
+    wh[2 * d] = A::decode(hi, false);
+    wh[2 * d + 1] = A::decode(hi, true);
+  }
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
+    uint4 xc[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) xc[cc] = xunit(b, cc);
+    const uint32_t x0[8] = {xc[0].x, xc[0].y, xc[0].z, xc[0].w, xc[1].x, xc[1].y, xc[1].z, xc[1].w};
+    const uint32_t x1[8] = {xc[2].x, xc[2].y, xc[2].z, xc[2].w, xc[3].x, xc[3].y, xc[3].z, xc[3].w};
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      p0 = A::dot(wl[t], x0[t], p0);
+      p1 = A::dot(wh[t], x1[t], p1);
+      p2 = A::dot(wl[t + 4], x0[t + 4], p2);
+      p3 = A::dot(wh[t + 4], x1[t + 4], p3);
+    }
+    acc[b] = __builtin_fmaf(s0, p0 + p2, acc[b]);
+    acc[b] = __builtin_fmaf(s1, p1 + p3, acc[b]);
+  }
+}
+
+// Activation layout in LDS: for activation row b and unit column ud (blocks P*ud ..
+// P*ud + P - 1), 4P consecutive 16-byte units (block-major, then 8-value chunk) plus
+// one padding unit, so a lane reads all of its unit's activations from one base
+// address with immediate offsets, and the lanes of a row (consecutive ud, stride
+// (4P+1)*16 bytes) hit distinct banks.
+template <int P>
+__device__ __forceinline__ int xs_index(int b, int ud, int nu, int B, int cc) {
+  return (b * nu + ud) * (4 * P + 1) + 4 * B + cc;
+}
+
+// `xu` points at the lane's first activation unit for this block column (row b = 0):
+// LDS unit (ud * (4P+1)) when XLDS, else the global address of block P*ud.
+template <int LAYOUT, int XT, int BATCH, bool XLDS, int P, int B>
+__device__ __forceinline__ void unit_block(const UnitRaw<P>& u, const uint4* xu, int xrow,
+                                           const uint16_t* xg, int64_t ldx, float (&acc)[BATCH]) {
+  float s0, s1;
+  unit_scales<LAYOUT, P, B>(u, s0, s1);
+  auto xunit = [&](int b, int cc) -> uint4 {
+    if constexpr (XLDS)
+      return xu[b * xrow + 4 * B + cc];
+    else
+      return *reinterpret_cast<const uint4*>(xg + b * ldx + 32 * B + 8 * cc);
+  };
+  block_dot<XT, BATCH>(unit_qs<LAYOUT, P, B>(u), s0, s1, xunit, acc);
+}
+
+template <int LAYOUT, int XT, int BATCH, bool XLDS, int P>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restrict__ w, int n,
-                                                        int nb, int log2cl, int groups,
+                                                        int nu, int log2cl, int groups, int gpw,
                                                         const uint16_t* __restrict__ x,
                                                         int64_t ldx, float* __restrict__ y,
                                                         int64_t ldy) {
-  typedef Act<XT> A;
-  typedef typename A::pair pair;
-  constexpr int BB = block_bytes(LAYOUT);
+  constexpr int UB = P * block_bytes(LAYOUT);  // bytes per unit
   extern __shared__ uint4 xs[];
-
-  if constexpr (XLDS) {
-    const int units = BATCH * 4 * nb;
-    for (int u = threadIdx.x; u < units; u += kThreads) {
-      const int j = u % nb;
-      const int bc = u / nb;
-      xs[u] = *reinterpret_cast<const uint4*>(x + (bc >> 2) * ldx + 32 * j + 8 * (bc & 3));
-    }
-    __syncthreads();
-  }
 
   const int lane = threadIdx.x & 63;
   const int cl = 1 << log2cl;
   const int rl = 64 >> log2cl;
   const int r_in = lane >> log2cl;
   const int c = lane & (cl - 1);
-  const int iters = nb >> log2cl;
-  const int wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * (kThreads / 64);
-  const int64_t rowbytes = static_cast<int64_t>(nb) * BB;
+  const int iters = nu >> log2cl;  // units per lane per row
+  // readfirstlane tells the compiler the wavefront index is uniform, so every cursor
+  // and loop bound derived from it lives in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
+  const int g_begin = wave * gpw;
+  const int g_end = min(g_begin + gpw, groups);
+  const int total = g_end > g_begin ? (g_end - g_begin) * iters : 0;  // units per lane
+  const int64_t rowbytes = static_cast<int64_t>(nu) * UB;  // < 2^31 / 64 (checked by the launcher)
 
-  for (int g = wave; g < groups; g += nwaves) {
-    const int row = g * rl + r_in;
-    float acc[BATCH];
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) acc[b] = 0.f;
-    if (row < n) {
-      const uint8_t* prow = w + row * rowbytes;
-#pragma unroll 2
-      for (int i = 0; i < iters; ++i) {
-        const int j = c + (i << log2cl);
-        const uint8_t* p = prow + j * BB;
-        const uint4 qv = load16(p);
-        uint32_t sw;
-        if constexpr (LAYOUT == kDual) {
-          uint16_t s2;
-          __builtin_memcpy(&s2, p + 16, 2);
-          sw = s2 & 0x7F7Fu;
-        } else {
-          sw = p[16] & 0x7Fu;
-        }
-        const uint32_t q[4] = {qv.x, qv.y, qv.z, qv.w};
-        pair wl[8], wh[8];  // first half (low nibbles), second half (high nibbles)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t lo = codes_low(q[d]);
-          const uint32_t hi = codes_high(q[d]);
-          wl[2 * d] = A::decode(lo, false);
-          wl[2 * d + 1] = A::decode(lo, true);
-          wh[2 * d] = A::decode(hi, false);
-          wh[2 * d + 1] = A::decode(hi, true);
-        }
-        const float s0 = e4m3_hw<0>(sw);
-        const float s1 = (LAYOUT == kDual) ? e4m3_hw<1>(sw) : s0;
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-          uint4 xc[4];
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            if constexpr (XLDS)
-              xc[cc] = xs[(b * 4 + cc) * nb + j];
-            else
-              xc[cc] = *reinterpret_cast<const uint4*>(x + b * ldx + 32 * j + 8 * cc);
-          }
-          const uint32_t x0[8] = {xc[0].x, xc[0].y, xc[0].z, xc[0].w,
-                                  xc[1].x, xc[1].y, xc[1].z, xc[1].w};
-          const uint32_t x1[8] = {xc[2].x, xc[2].y, xc[2].z, xc[2].w,
-                                  xc[3].x, xc[3].y, xc[3].z, xc[3].w};
-          float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            p0 = A::dot(wl[t], x0[t], p0);
-            p1 = A::dot(wh[t], x1[t], p1);
-          }
-          acc[b] = __builtin_fmaf(s0, p0, acc[b]);
-          acc[b] = __builtin_fmaf(s1, p1, acc[b]);
-        }
+  // Load cursor over (row group, unit index); wave-uniform. The address of the next
+  // unit is kept as a wave-uniform part (row group base + unit offset) plus a per-lane
+  // offset (row within the group, clamped to the last row, and lane column), so
+  // advancing the cursor costs scalar additions only.
+  int li = 0, issued = 0;
+  const int64_t group_stride = static_cast<int64_t>(rl) * rowbytes;
+  const int unit_stride = cl * UB;
+  const uint8_t* gbase = w + static_cast<int64_t>(g_begin) * group_stride;
+  int lane_off = min(r_in, max(n - 1 - g_begin * rl, 0)) * static_cast<int>(rowbytes) + c * UB;
+  int unit_off = 0;
+  int lg = g_begin;
+  auto load_next = [&](UnitRaw<P>& buf) {
+    if (issued < total) {
+      load_unit<LAYOUT, P>(gbase + unit_off + lane_off, buf);
+      ++issued;
+      unit_off += unit_stride;
+      if (++li == iters) {
+        li = 0;
+        unit_off = 0;
+        ++lg;
+        gbase += group_stride;
+        lane_off = min(r_in, max(n - 1 - lg * rl, 0)) * static_cast<int>(rowbytes) + c * UB;
       }
     }
-    for (int off = cl >> 1; off >= 1; off >>= 1) {
-#pragma unroll
-      for (int b = 0; b < BATCH; ++b) acc[b] += __shfl_xor(acc[b], off, 64);
+  };
+
+  // Three units in flight per lane: the first before the activations are staged (its
+  // latency overlaps theirs), the next two right after the barrier; each consumed unit
+  // is replaced by the next one, so decoding starts as soon as the first unit lands
+  // while the following ones stream in.
+  UnitRaw<P> r0, r1, r2;
+  load_next(r0);
+
+  if constexpr (XLDS) {
+    const int units = BATCH * 4 * nu * P;  // 16-byte activation units
+    for (int t = threadIdx.x; t < units; t += kThreads) {
+      const int cc = t & 3;
+      const int jb = t >> 2;  // block index over all activation rows
+      const int b = jb / (nu * P);
+      const int j = jb - b * nu * P;
+      xs[xs_index<P>(b, j / P, nu, j % P, cc)] =
+          *reinterpret_cast<const uint4*>(x + b * ldx + 32 * j + 8 * cc);
     }
-    if (c == 0 && row < n) {
+    __syncthreads();
+  }
+  load_next(r1);
+  load_next(r2);
+
+  float acc[BATCH];
 #pragma unroll
-      for (int b = 0; b < BATCH; ++b) y[b * ldy + row] = 0.5f * acc[b];
+  for (int b = 0; b < BATCH; ++b) acc[b] = 0.f;
+
+  // Compute cursor; wave-uniform. Activation pointers advance by whole unit columns.
+  int cg = g_begin, ci = 0;
+  const int xrow = nu * (4 * P + 1);  // LDS units per activation row
+  const uint4* xu0 = xs + c * (4 * P + 1);
+  const uint16_t* xg0 = x + 32 * P * c;
+  auto consume = [&](const UnitRaw<P>& u) {
+    const int row = cg * rl + r_in;
+    const uint4* xu = xu0 + ci * (cl * (4 * P + 1));
+    const uint16_t* xg = xg0 + ci * (32 * P * cl);
+    // Rows past n were loaded from a clamped address; their sums are never stored.
+    unit_block<LAYOUT, XT, BATCH, XLDS, P, 0>(u, xu, xrow, xg, ldx, acc);
+    if constexpr (P == 2) unit_block<LAYOUT, XT, BATCH, XLDS, P, 1>(u, xu, xrow, xg, ldx, acc);
+    if (++ci == iters) {  // row group complete: reduce over the CL lanes of each row
+      for (int off = cl >> 1; off >= 1; off >>= 1) {
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) acc[b] += __shfl_xor(acc[b], off, 64);
+      }
+      if (c == 0 && row < n) {
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) y[b * ldy + row] = 0.5f * acc[b];
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) acc[b] = 0.f;
+      ci = 0;
+      ++cg;
+    }
+  };
+
+  for (int t = 0; t < total; t += 3) {
+    consume(r0);
+    load_next(r0);
+    if (t + 1 < total) {
+      consume(r1);
+      load_next(r1);
+    }
+    if (t + 2 < total) {
+      consume(r2);
+      load_next(r2);
     }
   }
 }
 
+// CU count of the current device, queried once per device (a benign race: every
+// thread that races computes the same value).
 int device_cu_count() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return 256;
+    cus = 256;
+  if (dev < 64) cached[dev] = cus;
   return cus;
+}
+
+struct Plan {
+  int p, nu, log2cl, groups, gpw, wgs;
+};
+
+// Work plan for P consecutive blocks per lane unit.
+inline Plan make_plan(int p, int n, int nb, int waves_per_cu) {
+  Plan pl;
+  pl.p = p;
+  pl.nu = nb / p;
+  int g = 64;
+  while (pl.nu % g) g >>= 1;  // CL = gcd(64, units per row)
+  pl.log2cl = 0;
+  while ((1 << pl.log2cl) < g) ++pl.log2cl;
+  const int rl = 64 >> pl.log2cl;
+  pl.groups = (n + rl - 1) / rl;
+  const int max_waves = device_cu_count() * waves_per_cu;
+  pl.gpw = (pl.groups + max_waves - 1) / max_waves;  // row groups per wavefront
+  const int waves = (pl.groups + pl.gpw - 1) / pl.gpw;
+  pl.wgs = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  return pl;
 }
 
 template <int LAYOUT, int XT, int BATCH>
 hipError_t launch3(const uint8_t* w, int n, int nb, const uint16_t* x, int64_t ldx, float* y,
                    int64_t ldy, hipStream_t stream) {
-  int g = 64;
-  while (nb % g) g >>= 1;  // CL = gcd(64, nb); nb is a multiple of 8
-  int log2cl = 0;
-  while ((1 << log2cl) < g) ++log2cl;
-  const int rl = 64 >> log2cl;
-  const int groups = (n + rl - 1) / rl;
-  const int waves_per_wg = kThreads / 64;
-  int wgs = (groups + waves_per_wg - 1) / waves_per_wg;
-  const int cap = device_cu_count() * 8;
-  if (wgs > cap) wgs = cap;
-  const size_t xbytes = static_cast<size_t>(BATCH) * nb * 32 * 2;
-  if (xbytes <= static_cast<size_t>(kXLdsBudget)) {
-    gemv_kernel<LAYOUT, XT, BATCH, true><<<dim3(wgs), dim3(kThreads), xbytes, stream>>>(
-        w, n, nb, log2cl, groups, x, ldx, y, ldy);
-  } else {
-    gemv_kernel<LAYOUT, XT, BATCH, false><<<dim3(wgs), dim3(kThreads), 0, stream>>>(
-        w, n, nb, log2cl, groups, x, ldx, y, ldy);
+  // Activation bytes in LDS (largest unit size: 4P+1 units of 16 bytes per P blocks).
+  const size_t xbytes1 = static_cast<size_t>(BATCH) * nb * 5 * 16;
+  const size_t xbytes2 = static_cast<size_t>(BATCH) * (nb / 2) * 9 * 16;
+  const bool xlds = xbytes1 <= static_cast<size_t>(kXLdsBudget);
+  // Resident wavefronts per CU: the knob, capped by what LDS allows (160 KB per CU).
+  int waves_per_cu = RFP4_GEMV_WAVES_PER_CU;
+  if (xlds) {
+    const int wg_fit = static_cast<int>((160 * 1024) / xbytes1);
+    if (wg_fit * (kThreads / 64) < waves_per_cu) waves_per_cu = wg_fit * (kThreads / 64);
   }
+  // Pairs of blocks halve the per-block load instructions for the scale bytes; use them
+  // unless that leaves too few wavefronts to keep the CUs busy.
+  const Plan p2 = make_plan(2, n, nb, waves_per_cu);
+  const Plan p1 = make_plan(1, n, nb, waves_per_cu);
+  const int min_wgs = device_cu_count() * 3;  // >= 12 resident wavefronts per CU
+  const Plan pl = (p2.wgs >= min_wgs || p2.wgs >= p1.wgs) ? p2 : p1;
+  const dim3 grid(pl.wgs), block(kThreads);
+  const size_t shm = xlds ? (pl.p == 2 ? xbytes2 : xbytes1) : 0;
+#define RFP4_GEMV_LAUNCH(XL, PP)                                                               \
+  gemv_kernel<LAYOUT, XT, BATCH, XL, PP><<<grid, block, shm, stream>>>(w, n, pl.nu, pl.log2cl, \
+                                                                        pl.groups, pl.gpw, x, \
+                                                                        ldx, y, ldy)
+  if (xlds) {
+    if (pl.p == 2) RFP4_GEMV_LAUNCH(true, 2); else RFP4_GEMV_LAUNCH(true, 1);
+  } else {
+    if (pl.p == 2) RFP4_GEMV_LAUNCH(false, 2); else RFP4_GEMV_LAUNCH(false, 1);
+  }
+#undef RFP4_GEMV_LAUNCH
   return hipGetLastError();
 }
 

@@ -194,8 +194,12 @@ def test_gemv_extreme_values():
 
 @pytest.mark.parametrize("layout,dt", [(0, "f16"), (1, "bf16")])
 def test_gemv_exact_invariants(layout, dt):
-    """Toggling every index sign negates y bitwise; +1 on every scale exponent field
-    doubles y bitwise; two runs agree bitwise."""
+    """+1 on every scale exponent field doubles y bitwise (the scale enters through an
+    exact fp32 multiply); two runs agree bitwise (fixed reduction order, no atomics).
+    Toggling every index sign negates y to within rounding: the v_dot2_f32_{f16,bf16}
+    instructions that form the partial sums are not correctly rounded and not
+    sign-symmetric (measured on gfx950 against the exactly rounded sum), so an
+    exactly negated input can come back one fp32 ulp away from the negated output."""
     rng = np.random.default_rng(34 + layout)
     n, k = 200, 4096
     w = synth.weights(rng, layout, n, k)
@@ -208,7 +212,8 @@ def test_gemv_exact_invariants(layout, dt):
     flip = blocks.copy()
     flip[:, :, :16] ^= 0x88
     yf = run_gemv(flip.reshape(n, -1), layout, n, k, x)
-    assert np.array_equal(yf, -y)
+    _, den = O.gemv(w, layout, n, k, x64(x))
+    assert np.all(np.abs(yf.astype(np.float64) + y) <= 2.0 ** -20 * den)
     step = blocks.copy()
     step[:, :, 16:] += 8
     ys = run_gemv(step.reshape(n, -1), layout, n, k, x)
