@@ -319,17 +319,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
   }
 }
 
-// CU count of the current device, queried once per device (a benign race: every
-// thread that races computes the same value).
+// CU count of the current device, queried once per device and kept in an atomic
+// cache (threads that race store the same value).
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (dev < 64) cached[dev] = cus;
+  if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

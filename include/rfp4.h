@@ -23,8 +23,9 @@
  *
  * General rules for every entry point:
  *   - All pointers except rfp4_validate's `w_host` are device pointers. The caller
- *     owns every buffer; the library never allocates, frees or synchronizes and
- *     keeps no mutable global state, so calls from several threads are safe.
+ *     owns every buffer; the library never allocates, frees or synchronizes. Its
+ *     only global state is a per-device cache of the CU count and of one kernel
+ *     attribute, kept in atomics, so calls from several threads are safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are
  *     asynchronous and ordered on that stream; a fault in a kernel surfaces at the
  *     caller's next synchronization.
