@@ -7,24 +7,36 @@
 // scale is a bf16 value) and feeds v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
 // the epilogue rounds to bf16 (nearest even).
 //
-// Tiling. A 512-thread workgroup (8 wavefronts, two per SIMD) owns a 256 x 256 tile of
-// C (256 rows of A by 256 weight rows). Each step consumes 64 columns of K, i.e. two
-// ROCmFP4 blocks per weight row; each wavefront computes a 64 x 128 sub-tile as 2 x 4
-// MFMA tiles of 32 x 32, 128 fp32 accumulators per lane.
+// Tiling. The main configuration is a 512-thread workgroup (8 wavefronts, two per
+// SIMD) owning a 256 x 256 tile of C (256 rows of A by 256 weight rows); each
+// wavefront computes a 64 x 128 sub-tile as 2 x 4 MFMA tiles of 32 x 32 (128 fp32
+// accumulators per lane). Each step consumes 64 columns of K, i.e. two ROCmFP4 blocks
+// per weight row.
+//
+// Balance. A grid of equal tiles runs in whole rounds over the CUs, so 544 tiles on
+// 256 CUs would take three rounds for 2.125 rounds of work. The launcher therefore
+// splits the last columns of tiles into 128 x 64 pieces (a 256-thread configuration,
+// wavefronts of 64 x 32), run by a second launch, choosing the split with a cost model
+// of whole rounds of each kind.
 //
 // Pipeline (LDS double-buffered, one barrier per step). While step s is multiplied out
 // of LDS buffer s % 2:
 //   * the A tile of step s+1 is loaded into registers (four 16-byte chunks per thread)
 //     and written to the other buffer after the MFMAs;
-//   * the packed weights of step s+1 (loaded one step earlier, one block per thread)
-//     are decoded to bf16 into the other buffer, one 16-byte chunk per 16-column k slice,
-//     interleaved with that slice's MFMAs; the weights of step s+2 are loaded.
+//   * the packed weights of step s+1 (loaded one step earlier) are decoded to bf16 into
+//     the other buffer, one 16-byte chunk per 16-column k slice, interleaved with that
+//     slice's MFMAs; the weights of step s+2 are loaded.
 // LDS rows are 64 bf16 (eight 16-byte chunks) with the chunk index XOR-swizzled by the
 // row, so the MFMA fragment reads (32 consecutive rows, one chunk) hit distinct banks.
 //
 // Mapping. Workgroups are dispatched round-robin over the 8 XCDs; with the M-tile index
-// taken as (workgroup id mod M-tiles), all workgroups of an XCD share the same 256 rows
-// of A (2.6 MB at K = 5120), which stay in that XCD's L2.
+// taken as (workgroup id mod M-tiles), the workgroups of an XCD share a few row slabs
+// of A (2.6 MB per 256 rows at K = 5120), which stay in that XCD's L2.
+
+#include <stdlib.h>
+#include <string.h>
+
+#include <type_traits>
 
 #include "rfp4_decode.h"
 #include "rfp4_internal.h"
@@ -35,18 +47,97 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256;
-constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int kThreads = 512;
-constexpr int kTileBytes = BM * BK * 2;  // one bf16 tile of A or W in LDS (32 KB)
 
-// Byte offset of 16-byte chunk c (0..7) of row r in a swizzled LDS tile.
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// Weight decode through a per-workgroup table in LDS (1) or with converts and
+// multiplies (0); see decode_chunk.
+#ifndef RFP4_GEMM_LUT
+#define RFP4_GEMM_LUT 1
+#endif
+
+// Tile configuration: BM x BN tile of C per workgroup, WM x WN wavefronts.
+template <int BM_, int BN_, int WM_, int WN_, int PD_ = 1, bool PP_ = false>
+struct TileCfg {
+  static constexpr int BM = BM_;
+  static constexpr int BN = BN_;
+  static constexpr int WM = WM_;
+  static constexpr int WN = WN_;
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWaveM = BM / WM;  // rows of C per wavefront
+  static constexpr int kWaveN = BN / WN;  // columns of C per wavefront
+  static constexpr int TM = kWaveM / 32;  // MFMA tiles per wavefront along M
+  static constexpr int TN = kWaveN / 32;  // ... and along N
+  static constexpr int kARows = kThreads / 8;   // A rows loaded per pass
+  static constexpr int kAPasses = BM / kARows;  // 16-byte A chunks per thread per step
+  static constexpr int kAPrefetch = PD_;        // steps of A in flight in registers
+  static constexpr bool kPingPong = PP_;        // two-phase schedule (see the kernel)
+  static constexpr int kBlocks = 2 * BN;        // weight blocks per 64-column step
+  // Each thread decodes kBlocksPerThread whole blocks, or a half or a quarter of a
+  // block when there are two or four times as many threads as blocks (kDecThreads).
+  static constexpr int kBlocksPerThread = kBlocks > kThreads ? kBlocks / kThreads : 1;
+  static constexpr int kDecThreads = kBlocks < kThreads ? kThreads / kBlocks : 1;
+  static constexpr int kChunksPerBlock = 4 / kDecThreads;  // 16-byte chunks per block share
+  static constexpr int kChunks = kBlocksPerThread * kChunksPerBlock;
+  static constexpr int kABytes = BM * BK * 2;
+  static constexpr int kWBytes = BN * BK * 2;
+  static constexpr int kLutOffset = 2 * (kABytes + kWBytes);
+  static constexpr int kLdsBytes = kLutOffset + (RFP4_GEMM_LUT ? 128 * 16 : 0);
+  static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wavefront tile is whole MFMA tiles");
+  static_assert(kARows % 16 == 0 && BM % kARows == 0 && kAPasses <= 8, "A loader shape");
+  static_assert(kBlocks % kThreads == 0 || kThreads % kBlocks == 0, "decode split");
+  static_assert(kDecThreads <= 4 && kBlocksPerThread <= 2, "decode split");
+  static_assert(kAPrefetch == 1 || kAPrefetch == 2 || kAPrefetch == 4, "A prefetch depth");
+  static_assert(kDecThreads == 1 || kBlocks % 64 == 0, "decode group uniform per wavefront");
+  static_assert(kWaveM % 16 == 0 && kWaveN % 16 == 0, "fragment rows share a swizzle term");
+  // Fragment reads use one base register per k slice and operand, plus an immediate
+  // (buffer offset + tile row offset) when that fits the 16-bit field, else one base
+  // register per buffer as well.
+  static constexpr bool kSplitA = kABytes + (TM - 1) * 32 * 128 >= 65536;
+  static constexpr bool kSplitW = kWBytes + (TN - 1) * 32 * 128 >= 65536;
+};
+
+// Main tiles: 0 = 256 x 256 with eight wavefronts (two per SIMD, 64 x 128 each);
+// 1 = 512 x 128 with eight wavefronts (128 x 64 each; half the decode per flop);
+// 2 = 256 x 256 with four wavefronts (one per SIMD, 128 x 128 each).
+#ifndef RFP4_GEMM_MAIN
+#define RFP4_GEMM_MAIN 0
+#endif
+#ifndef RFP4_GEMM_MAIN_PD
+#define RFP4_GEMM_MAIN_PD 1
+#endif
+#ifndef RFP4_GEMM_PINGPONG
+#define RFP4_GEMM_PINGPONG 1
+#endif
+using MainCfg = std::conditional_t<
+    RFP4_GEMM_MAIN == 1, TileCfg<512, 128, 4, 2, RFP4_GEMM_MAIN_PD>,
+    std::conditional_t<RFP4_GEMM_MAIN == 2, TileCfg<256, 256, 2, 2, RFP4_GEMM_MAIN_PD>,
+                       std::conditional_t<RFP4_GEMM_PINGPONG != 0, TileCfg<256, 256, 4, 2, 2, true>,
+                                          TileCfg<256, 256, 4, 2, RFP4_GEMM_MAIN_PD>>>>;
+// Tail pieces: 0 = 128 x 64, four wavefronts (64 x 32 each); 1 = 128 x 64, eight
+// wavefronts (32 x 32 each); 2 = 64 x 64, four wavefronts (32 x 32 each); 3 = 128 x 32,
+// four wavefronts (32 x 32 each). RFP4_GEMM_TAIL_PD: steps of A prefetched.
+#ifndef RFP4_GEMM_TAIL
+#define RFP4_GEMM_TAIL 0
+#endif
+#ifndef RFP4_GEMM_TAIL_PD
+#define RFP4_GEMM_TAIL_PD 2
+#endif
+using TailCfg = std::conditional_t<
+    RFP4_GEMM_TAIL == 1, TileCfg<128, 64, 4, 2, RFP4_GEMM_TAIL_PD>,
+    std::conditional_t<
+        RFP4_GEMM_TAIL == 2, TileCfg<64, 64, 2, 2, RFP4_GEMM_TAIL_PD>,
+        std::conditional_t<RFP4_GEMM_TAIL == 3, TileCfg<128, 32, 4, 1, RFP4_GEMM_TAIL_PD>,
+                           TileCfg<128, 64, 2, 2, RFP4_GEMM_TAIL_PD>>>>;
+
+// LDS tiles are rows of 64 bf16 (128 bytes, eight 16-byte chunks); chunk c of row r
+// is stored at chunk position c ^ ((r >> 1) & 7). A 16-byte access by 16 lanes covers
+// 256 bytes of banks; with this swizzle the fragment reads (16 consecutive rows, one
+// chunk), the A stores (two rows, eight chunks) and the weight stores (eight rows,
+// chunks {c, c + 4}) all fall on distinct banks.
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   // Both values are exactly representable in bf16, so the conversion is exact.
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
   return __builtin_bit_cast(uint32_t, v);
 }
@@ -78,176 +169,569 @@ __device__ __forceinline__ BlockRaw load_block(const uint8_t* p) {
   return b;
 }
 
-// Decode chunk c (weights 8c .. 8c+7) of one block to bf16 (c * S, exact) and write it
-// to chunk c0 + c of LDS row r. Chunks 0, 1 are the low nibbles of qs words 2c, 2c+1
-// (first half, scale e0); chunks 2, 3 the high nibbles of qs words 2(c-2), 2(c-2)+1
-// (second half, scale e1; the fast layout has one scale).
+#ifndef RFP4_GEMM_HW_SCALE
+#define RFP4_GEMM_HW_SCALE 1
+#endif
+
+// Chunk C (weights 8C .. 8C+7) of one block as eight bf16 values c * S (exact).
+// Chunks 0, 1 are the low nibbles of qs words 2C, 2C+1 (first half, scale e0);
+// chunks 2, 3 the high nibbles of qs words 2(C-2), 2(C-2)+1 (second half, scale e1;
+// the fast layout has one scale).
+//
+// The scale is taken either from the integer bit formula (any byte) or, for validated
+// weights, from the hardware E4M3 converter applied to the byte's low seven bits, with
+// codes of half-weights (the converter gives twice the decoded scale).
+//
+// Table decode: for each of the 128 values of a scale byte's low seven bits the table
+// holds the bf16 encodings of the eight magnitudes times the decoded scale (exact), as
+// a plane of low bytes (entries 0-3, 4-7) and a plane of high bytes. Four weights then
+// take two v_perm_b32 that gather their low and high bytes by magnitude index, an OR
+// of the sign bits into the high bytes (index 8 gives -0.0, harmless in the products)
+// and two v_perm_b32 that interleave the planes into bf16 pairs.
 template <int LAYOUT, int C>
-__device__ __forceinline__ void decode_chunk_to_lds(const BlockRaw& b, char* tile, int r, int c0) {
-  const float s = scale_exact((C < 2 || LAYOUT == kFast) ? (b.sc & 0xFFu) : (b.sc >> 8));
+__device__ __forceinline__ uint4 decode_chunk_table(const BlockRaw& b, const uint4& t) {
   const uint32_t q[4] = {b.qs.x, b.qs.y, b.qs.z, b.qs.w};
   uint32_t o[4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t word = q[2 * (C & 1) + h];
+    const uint32_t sel = (C < 2) ? (word & 0x07070707u) : ((word >> 4) & 0x07070707u);
+    const uint32_t sign = (C < 2) ? ((word << 4) & 0x80808080u) : (word & 0x80808080u);
+    const uint32_t lo = __builtin_amdgcn_perm(t.y, t.x, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(t.w, t.z, sel) | sign;
+    o[2 * h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    o[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
+template <int LAYOUT, int C>
+__device__ __forceinline__ uint4 decode_chunk(const BlockRaw& b, const uint4* tabs) {
+#if RFP4_GEMM_LUT
+  return decode_chunk_table<LAYOUT, C>(b, tabs[(C < 2 || LAYOUT == kFast) ? 0 : 1]);
+#endif
+  constexpr bool kFirst = C < 2 || LAYOUT == kFast;
+#if RFP4_GEMM_HW_SCALE
+  const uint32_t sc7 = b.sc & 0x7F7Fu;
+  const float s = kFirst ? e4m3_hw<0>(sc7) : e4m3_hw<1>(sc7);
+#else
+  const float s = scale_exact(kFirst ? (b.sc & 0xFFu) : (b.sc >> 8));
+#endif
+  const uint32_t q[4] = {b.qs.x, b.qs.y, b.qs.z, b.qs.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t word = q[2 * (C & 1) + h];
+#if RFP4_GEMM_HW_SCALE
+    const uint32_t codes = (C < 2) ? half_codes_low(word) : half_codes_high(word);
+#else
     const uint32_t codes = (C < 2) ? codes_low(word) : codes_high(word);
+#endif
     const f32x2 lo = pair_f32(codes, false);
     const f32x2 hi = pair_f32(codes, true);
     o[2 * h] = pack_bf16(lo.x * s, lo.y * s);
     o[2 * h + 1] = pack_bf16(hi.x * s, hi.y * s);
   }
-  *reinterpret_cast<uint4*>(tile + swz(r, c0 + C)) = uint4{o[0], o[1], o[2], o[3]};
+  return uint4{o[0], o[1], o[2], o[3]};
 }
 
-template <int LAYOUT>
-__device__ __forceinline__ void decode_block_to_lds(const BlockRaw& b, char* tile, int r, int c0) {
-  decode_chunk_to_lds<LAYOUT, 0>(b, tile, r, c0);
-  decode_chunk_to_lds<LAYOUT, 1>(b, tile, r, c0);
-  decode_chunk_to_lds<LAYOUT, 2>(b, tile, r, c0);
-  decode_chunk_to_lds<LAYOUT, 3>(b, tile, r, c0);
+// Chunk CL of this thread's share of a block, stored at dst. With one thread per
+// block the share is chunks 0..3; with two, group g owns chunks 2g, 2g + 1; with four,
+// group g owns chunk g (the group is uniform over a wavefront).
+template <int LAYOUT, typename Cfg, int CL>
+__device__ __forceinline__ void decode_part(const BlockRaw& b, const uint4* tabs, char* dst,
+                                            int grp) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  if constexpr (Cfg::kDecThreads == 1) {
+    *d = decode_chunk<LAYOUT, CL>(b, tabs);
+  } else if constexpr (Cfg::kDecThreads == 2) {
+    if (grp == 0)
+      *d = decode_chunk<LAYOUT, CL>(b, tabs);
+    else
+      *d = decode_chunk<LAYOUT, CL + 2>(b, tabs);
+  } else {
+    if (grp == 0)
+      *d = decode_chunk<LAYOUT, 0>(b, tabs);
+    else if (grp == 1)
+      *d = decode_chunk<LAYOUT, 1>(b, tabs);
+    else if (grp == 2)
+      *d = decode_chunk<LAYOUT, 2>(b, tabs);
+    else
+      *d = decode_chunk<LAYOUT, 3>(b, tabs);
+  }
 }
 
-template <int LAYOUT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restrict__ w, int n,
-                                                        int nb, const uint16_t* __restrict__ a,
-                                                        int m, int64_t lda,
-                                                        uint16_t* __restrict__ c, int64_t ldc,
-                                                        int m_tiles) {
+// One workgroup computes tile (blockIdx.x mod m_tiles, blockIdx.x / m_tiles) of the
+// region of C whose columns start at n_base; rows and columns outside [0, m) x [0, n)
+// are computed on clamped inputs and never stored. `steps` (= k / 64) must be even.
+template <int LAYOUT, typename Cfg>
+__global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __restrict__ w,
+                                                             int n, int nb,
+                                                             const uint16_t* __restrict__ a,
+                                                             int m, int64_t lda,
+                                                             uint16_t* __restrict__ c,
+                                                             int64_t ldc, int m_tiles,
+                                                             int64_t n_base) {
   constexpr int BB = block_bytes(LAYOUT);
+  constexpr int TM = Cfg::TM;
+  constexpr int TN = Cfg::TN;
+  // LDS: A buffers 0 and 1, then W buffers 0 and 1, so that every fragment read is one
+  // of a few per-lane base registers plus an immediate offset below 64 KB.
+  constexpr int kW0 = 2 * Cfg::kABytes;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // Buffer b of the A tile at smem + 2b * kTileBytes, of the W tile one tile later.
-  auto a_tile = [&](int b) { return smem + 2 * b * kTileBytes; };
-  auto w_tile = [&](int b) { return smem + (2 * b + 1) * kTileBytes; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 1;  // 0..3: 64-row slab of the tile
-  const int wn = wid & 1;   // 0..1: 128-column slab
+  const int wm = wid / Cfg::WN;
+  const int wn = wid % Cfg::WN;
   const int tile_id = blockIdx.x;
-  const int m0 = (tile_id % m_tiles) * BM;
-  const int n0 = (tile_id / m_tiles) * BN;
+  const int m0 = (tile_id % m_tiles) * Cfg::BM;
+  const int64_t n0 = n_base + static_cast<int64_t>(tile_id / m_tiles) * Cfg::BN;
   const int64_t rowbytes = static_cast<int64_t>(nb) * BB;
   const int steps = nb / 2;  // BK = 64 = two blocks
 
-  // A loader: thread -> 16-byte chunk (t % 8) of rows t/8 + 64 i, i = 0..3 (eight
-  // threads cover a row's 128 contiguous bytes); staged in registers, written to the
-  // swizzled LDS tile after the MFMAs of the current step.
+  // A loader: thread -> 16-byte chunk (t % 8) of rows t/8 + kARows * i (eight threads
+  // cover a row's 128 contiguous bytes); staged in registers, written to the swizzled
+  // LDS tile after the MFMAs of the current step. kARows is a multiple of 16, so the
+  // rows of a thread share one swizzle term.
+  constexpr int AP = Cfg::kAPasses;
   const int a_row0 = tid >> 3;
   const int a_chunk = tid & 7;
   struct AChunks {
-    uint4 v0, v1, v2, v3;
+    uint4 v[AP];
   };
-  const uint16_t* a_col = a + a_chunk * 8;
-  auto a_row_ptr = [&](int i) { return a_col + min(m0 + a_row0 + 64 * i, m - 1) * lda; };
-  // Rows past m are clamped to row m - 1; their results are never stored.
-  const uint16_t* a_p0 = a_row_ptr(0);
-  const uint16_t* a_p1 = a_row_ptr(1);
-  const uint16_t* a_p2 = a_row_ptr(2);
-  const uint16_t* a_p3 = a_row_ptr(3);
+  const uint16_t* a_p[AP];
+#pragma unroll
+  for (int i = 0; i < AP; ++i)  // rows past m are clamped to row m - 1, never stored
+    a_p[i] = a + a_chunk * 8 + min(m0 + a_row0 + Cfg::kARows * i, m - 1) * lda;
   auto load_a = [&](int s) {
     AChunks r;
-    r.v0 = *reinterpret_cast<const uint4*>(a_p0 + s * BK);
-    r.v1 = *reinterpret_cast<const uint4*>(a_p1 + s * BK);
-    r.v2 = *reinterpret_cast<const uint4*>(a_p2 + s * BK);
-    r.v3 = *reinterpret_cast<const uint4*>(a_p3 + s * BK);
+#pragma unroll
+    for (int i = 0; i < AP; ++i) r.v[i] = *reinterpret_cast<const uint4*>(a_p[i] + s * BK);
     return r;
   };
-  auto store_a = [&](const AChunks& r, char* tile) {
-    *reinterpret_cast<uint4*>(tile + swz(a_row0, a_chunk)) = r.v0;
-    *reinterpret_cast<uint4*>(tile + swz(a_row0 + 64, a_chunk)) = r.v1;
-    *reinterpret_cast<uint4*>(tile + swz(a_row0 + 128, a_chunk)) = r.v2;
-    *reinterpret_cast<uint4*>(tile + swz(a_row0 + 192, a_chunk)) = r.v3;
+  char* const a_st = smem + a_row0 * 128 + (swz_chunk(a_row0, a_chunk) << 4);
+  auto store_a = [&](const AChunks& r, int buf) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i)
+      *reinterpret_cast<uint4*>(a_st + buf * Cfg::kABytes + i * Cfg::kARows * 128) = r.v[i];
   };
-  // W loader: thread -> (weight row, block of the step).
-  const int w_r = tid >> 1;
-  const int w_blk = tid & 1;
-  const uint8_t* w_row = w + min(n0 + w_r, n - 1) * rowbytes + w_blk * BB;
-  auto load_w = [&](int s) { return load_block<LAYOUT>(w_row + s * 2 * BB); };
 
-  f32x16 acc[2][4];
+  // W loader: thread -> blocks w_idx + kThreads q (q < kBlocksPerThread) of the step;
+  // block index bi covers weight row bi / 2, block bi % 2 of the step (columns
+  // 32 (bi % 2) .. 32 (bi % 2) + 31 of the 64).
+  constexpr int BP = Cfg::kBlocksPerThread;
+  constexpr int CPB = Cfg::kChunksPerBlock;
+  const int w_idx = tid % Cfg::kBlocks;
+  const int w_grp = __builtin_amdgcn_readfirstlane(tid / Cfg::kBlocks);
+  const uint8_t* w_row[BP];
+  char* w_st[BP][CPB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int q = 0; q < BP; ++q) {
+    const int bi = w_idx + Cfg::kThreads * q;
+    const int r = bi >> 1;
+    const int blk = bi & 1;
+    w_row[q] = w + min(n0 + r, static_cast<int64_t>(n) - 1) * rowbytes + blk * BB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < CPB; ++j) {
+      const int cc = 4 * blk + w_grp * CPB + j;  // chunk of the 64-column LDS row
+      w_st[q][j] = smem + kW0 + r * 128 + (swz_chunk(r, cc) << 4);
+    }
+  }
+  struct WRaw {
+    BlockRaw b[BP];
+  };
+  auto load_w = [&](int s) {
+    WRaw r;
+#pragma unroll
+    for (int q = 0; q < BP; ++q) r.b[q] = load_block<LAYOUT>(w_row[q] + s * 2 * BB);
+    return r;
+  };
+  // Decode tables of the scale bytes of this thread's blocks (entries e0, e1).
+  struct WTab {
+    uint4 t[BP][2];
+  };
+  auto load_tabs = [&](const WRaw& wr) {
+    WTab r;
+#pragma unroll
+    for (int q = 0; q < BP; ++q) {
+#if RFP4_GEMM_LUT
+      const uint32_t sc = wr.b[q].sc;
+      const char* lut = smem + Cfg::kLutOffset;
+      r.t[q][0] = *reinterpret_cast<const uint4*>(lut + ((sc & 0x7Fu) << 4));
+      r.t[q][1] = LAYOUT == kDual ? *reinterpret_cast<const uint4*>(lut + (((sc >> 8) & 0x7Fu) << 4))
+                                  : r.t[q][0];
+#else
+      r.t[q][0] = r.t[q][1] = uint4{0u, 0u, 0u, 0u};
+#endif
+    }
+    return r;
+  };
+  // Local chunk J = q * CPB + j of this thread's decode work for one step.
+  auto decode_to = [&](const WRaw& wr, const WTab& tb, int buf, auto j_c) {
+    constexpr int J = decltype(j_c)::value;
+    constexpr int q = J / CPB;
+    constexpr int j = J % CPB;
+    decode_part<LAYOUT, Cfg, j>(wr.b[q], tb.t[q], w_st[q][j] + buf * Cfg::kWBytes, w_grp);
+  };
+  // The local chunks decoded alongside k slice kk: [kk C / 4, (kk + 1) C / 4) with C =
+  // kChunks, so the decode work is spread evenly over the four slices of a step.
+  auto decode_slot = [&](const WRaw& wr, const WTab& tb, int buf, auto kk_c) {
+    constexpr int kk = decltype(kk_c)::value;
+    constexpr int J0 = kk * Cfg::kChunks / 4;
+    constexpr int J1 = (kk + 1) * Cfg::kChunks / 4;
+    static_assert(J1 - J0 <= 2, "at most two chunks per k slice");
+    if constexpr (J0 < J1) decode_to(wr, tb, buf, std::integral_constant<int, J0>{});
+    if constexpr (J0 + 1 < J1) decode_to(wr, tb, buf, std::integral_constant<int, J0 + 1>{});
+  };
 
-  // Prologue: stage 0 in LDS, the weights of stage 1 in registers.
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  // A in flight: with prefetch depth PD > 1, the A chunks of step s + PD are loaded
+  // into ring slot s % PD at the start of step s, and slot (s + 1) % PD (stage s + 1)
+  // is written to LDS at its end.
+  constexpr int PD = Cfg::kAPrefetch;
+  AChunks a_ring[PD];
+
+  // Prologue: stage 0 in LDS, the weights of stage 1 and the A chunks of stages
+  // 1 .. PD - 1 in registers.
   {
     const AChunks a0 = load_a(0);
-    const BlockRaw b0 = load_w(0);
-    store_a(a0, a_tile(0));
-    decode_block_to_lds<LAYOUT>(b0, w_tile(0), w_r, 4 * w_blk);
+    const WRaw b0 = load_w(0);
+#if RFP4_GEMM_LUT
+    // Decode table: entry e (the low seven bits of a scale byte) holds bf16(m * S(e))
+    // for the magnitudes m = 0, 1, 2, 3, 4, 6, 8, 10 as a low-byte and a high-byte
+    // plane. Every product is exactly representable, so truncating fp32 is exact.
+    if (tid < 128) {
+      const float sv = scale_exact(static_cast<uint32_t>(tid));
+      const float mags[8] = {0.f, 1.f, 2.f, 3.f, 4.f, 6.f, 8.f, 10.f};
+      uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t bits = __float_as_uint(mags[i] * sv) >> 16;
+        lo[i >> 2] |= (bits & 0xFFu) << (8 * (i & 3));
+        hi[i >> 2] |= (bits >> 8) << (8 * (i & 3));
+      }
+      *reinterpret_cast<uint4*>(smem + Cfg::kLutOffset + 16 * tid) = uint4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    __syncthreads();
+#endif
+    const WTab t0 = load_tabs(b0);
+    store_a(a0, 0);
+    decode_slot(b0, t0, 0, std::integral_constant<int, 0>{});
+    decode_slot(b0, t0, 0, std::integral_constant<int, 1>{});
+    decode_slot(b0, t0, 0, std::integral_constant<int, 2>{});
+    decode_slot(b0, t0, 0, std::integral_constant<int, 3>{});
   }
-  BlockRaw w_next = load_w(min(1, steps - 1));
+  WRaw w_next = load_w(min(1, steps - 1));
+#pragma unroll
+  for (int p = 1; p < PD; ++p) a_ring[p] = load_a(min(p, steps - 1));
   __syncthreads();
 
-  const int fr = lane & 31;  // fragment row within a 32-row MFMA tile
-  const int fk = lane >> 5;  // which 8-column half of a 16-column k slice
-  // Branch-free main loop: on the last step the prefetches below are clamped to the
-  // last stage and only refill the buffer that is no longer read.
-  for (int s = 0; s < steps; ++s) {
-    const int cur = s & 1;
+  // Fragment addresses. Lane (fr, fk) reads row fr of each 32-row MFMA tile and the
+  // 8-column half fk of a 16-column k slice kk, i.e. logical chunk 2 kk + fk. The rows
+  // of a lane's fragments differ by multiples of 16 and share the swizzle term.
+  const int fr = lane & 31;
+  const int fk = lane >> 5;
+  constexpr int NBA = Cfg::kSplitA ? 2 : 1;
+  constexpr int NBW = Cfg::kSplitW ? 2 : 1;
+  const char* a_frag[NBA][4];
+  const char* w_frag[NBW][4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int pc = swz_chunk(fr, 2 * kk + fk) << 4;
+#pragma unroll
+    for (int bu = 0; bu < NBA; ++bu)
+      a_frag[bu][kk] = smem + bu * Cfg::kABytes + (wm * Cfg::kWaveM + fr) * 128 + pc;
+#pragma unroll
+    for (int bu = 0; bu < NBW; ++bu)
+      w_frag[bu][kk] = smem + kW0 + bu * Cfg::kWBytes + (wn * Cfg::kWaveN + fr) * 128 + pc;
+  }
+
+  // One step: multiply stage `cur` out of LDS while the next stage is prepared in the
+  // other buffer. The loop below runs two steps per iteration so that the buffer index
+  // is a compile-time constant and every LDS address is a base register plus an
+  // immediate. On the last steps the prefetches are clamped to the last stage and only
+  // refill the buffer that is no longer read.
+  auto step = [&](auto u_c, int s) {
+    constexpr int U = decltype(u_c)::value;  // s mod the unroll factor
+    constexpr int cur = U & 1;
     // Issue order matters: the A loads first and the weight loads after them, so that
-    // storing A at the end of the step waits only for the A loads (vmcnt counts in issue
-    // order); the scheduling barrier keeps the compiler from sinking the loads.
-    const AChunks a_next = load_a(min(s + 1, steps - 1));
-    const BlockRaw w_after = load_w(min(s + 2, steps - 1));  // two steps ahead
+    // storing A at the end of the step waits only for the A loads (vmcnt counts in
+    // issue order); the scheduling barrier keeps the compiler from sinking the loads.
+    a_ring[U % PD] = load_a(min(s + PD, steps - 1));
+    const WRaw w_after = load_w(min(s + 2, steps - 1));  // two steps ahead
     __builtin_amdgcn_sched_barrier(0);
-    const char* at = a_tile(cur);
-    const char* wt = w_tile(cur);
-    char* wn_tile = w_tile(cur ^ 1);
-    bf16x8 af[2][2], bfr[2][4];
+    const WTab tn = load_tabs(w_next);
+    bf16x8 af[2][TM], bfr[2][TN];
     auto load_frags = [&](int kk, int slot) {
-      const int ck = 2 * kk + fk;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[slot][i] = *reinterpret_cast<const bf16x8*>(at + swz(wm * 64 + i * 32 + fr, ck));
+      for (int i = 0; i < TM; ++i)
+        af[slot][i] = *reinterpret_cast<const bf16x8*>(
+            Cfg::kSplitA ? a_frag[NBA - 1 < cur ? 0 : cur][kk] + i * 32 * 128
+                         : a_frag[0][kk] + cur * Cfg::kABytes + i * 32 * 128);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[slot][j] = *reinterpret_cast<const bf16x8*>(wt + swz(wn * 128 + j * 32 + fr, ck));
+      for (int j = 0; j < TN; ++j)
+        bfr[slot][j] = *reinterpret_cast<const bf16x8*>(
+            Cfg::kSplitW ? w_frag[NBW - 1 < cur ? 0 : cur][kk] + j * 32 * 128
+                         : w_frag[0][kk] + cur * Cfg::kWBytes + j * 32 * 128);
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][i], bfr[slot][j], acc[i][j], 0, 0, 0);
     };
-    // k slice kk: fragments of kk+1 are read while the MFMAs of kk run, and one
-    // 16-byte chunk of the next stage's weights is decoded alongside.
+    // k slice kk: fragments of kk+1 are read while the MFMAs of kk run, and a share of
+    // the next stage's weights is decoded alongside.
+    // Scheduling fences keep this order: the fragments of slice kk + 1 are read before
+    // the MFMAs of slice kk are issued, so each read has a whole slice of MFMAs to land
+    // (left alone, the compiler moves the reads next to their uses and exposes the LDS
+    // latency once per slice).
+#ifndef RFP4_GEMM_FENCE
+#define RFP4_GEMM_FENCE 1
+#endif
+    auto fence = [&]() {
+      if constexpr (RFP4_GEMM_FENCE != 0 || TM * TN >= 16) __builtin_amdgcn_sched_barrier(0);
+    };
     load_frags(0, 0);
     load_frags(1, 1);
+    fence();
     mfmas(0);
-    decode_chunk_to_lds<LAYOUT, 0>(w_next, wn_tile, w_r, 4 * w_blk);
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 0>{});
+    fence();
     load_frags(2, 0);
+    fence();
     mfmas(1);
-    decode_chunk_to_lds<LAYOUT, 1>(w_next, wn_tile, w_r, 4 * w_blk);
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 1>{});
+    fence();
     load_frags(3, 1);
+    fence();
     mfmas(0);
-    decode_chunk_to_lds<LAYOUT, 2>(w_next, wn_tile, w_r, 4 * w_blk);
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 2>{});
+    fence();
     mfmas(1);
-    decode_chunk_to_lds<LAYOUT, 3>(w_next, wn_tile, w_r, 4 * w_blk);
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 3>{});
     __builtin_amdgcn_sched_barrier(0);
-    store_a(a_next, a_tile(cur ^ 1));
+    store_a(a_ring[(U + 1) % PD], cur ^ 1);
     w_next = w_after;
     __syncthreads();
+  };
+  // Ping-pong schedule (eight wavefronts, two per SIMD). Waves 0-3 and 4-7 sit on the
+  // same four SIMDs; each step has two phases separated by barriers. In one phase a
+  // group issues its 32 MFMAs on stage s (fragments read one slice ahead) while the
+  // other group prepares its half of stage s + 1 (A chunks and decoded weights into the
+  // other buffer, loads for later stages); in the next phase the roles swap. The MFMA
+  // pipe of every SIMD is fed by one wave while the other issues VALU and memory work.
+  // The weight rows and A rows a thread prepares lie in its group's half of the tile
+  // (thread t handles weight row t / 2 and A rows t / 8 + kARows i).
+#ifndef RFP4_GEMM_SETPRIO
+#define RFP4_GEMM_SETPRIO 1
+#endif
+  auto mfma_block = [&](auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    // The wave issuing MFMAs takes issue priority over its SIMD partner's VALU work.
+    if constexpr (RFP4_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto load_frags = [&](int kk, int slot) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[slot][i] = *reinterpret_cast<const bf16x8*>(
+            Cfg::kSplitA ? a_frag[NBA - 1 < cur ? 0 : cur][kk] + i * 32 * 128
+                         : a_frag[0][kk] + cur * Cfg::kABytes + i * 32 * 128);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[slot][j] = *reinterpret_cast<const bf16x8*>(
+            Cfg::kSplitW ? w_frag[NBW - 1 < cur ? 0 : cur][kk] + j * 32 * 128
+                         : w_frag[0][kk] + cur * Cfg::kWBytes + j * 32 * 128);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][i], bfr[slot][j], acc[i][j], 0, 0, 0);
+    };
+    load_frags(0, 0);
+    load_frags(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (RFP4_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  // Prepare stage s + 1 in buffer (s + 1) % 2: loads for A(s + PD) and W(s + 2) are
+  // issued first, then A(s + 1) (loaded PD - 1 steps earlier) is stored and W(s + 1)
+  // (loaded one step earlier) decoded.
+  auto prep_block = [&](auto u_c, int s) {
+    constexpr int U = decltype(u_c)::value;
+    constexpr int cur = U & 1;
+    a_ring[U % PD] = load_a(min(s + PD, steps - 1));
+    const WRaw w_after = load_w(min(s + 2, steps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    const WTab tn = load_tabs(w_next);
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 0>{});
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 1>{});
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 2>{});
+    decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 3>{});
+    store_a(a_ring[(U + 1) % PD], cur ^ 1);
+    w_next = w_after;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Each group runs its own straight-line loop; both loops execute the same sequence
+  // of workgroup barriers (two per step), which pairs them phase by phase.
+  auto pp_step = [&](auto u_c, int s, auto second_c) {
+    constexpr int U = decltype(u_c)::value;
+    constexpr auto cur_c = std::integral_constant<int, (U & 1)>{};
+#ifndef RFP4_GEMM_MID_BARRIER
+#define RFP4_GEMM_MID_BARRIER 1
+#endif
+    if constexpr (!decltype(second_c)::value) {
+      mfma_block(cur_c);
+      if constexpr (RFP4_GEMM_MID_BARRIER) __syncthreads();
+      prep_block(u_c, s);
+      __syncthreads();
+    } else {
+      prep_block(u_c, s);
+      if constexpr (RFP4_GEMM_MID_BARRIER) __syncthreads();
+      mfma_block(cur_c);
+      __syncthreads();
+    }
+  };
+
+  // steps is a multiple of 4 (k % 256 == 0).
+  if constexpr (Cfg::kPingPong) {
+    static_assert(PD == 2, "the ping-pong schedule keeps two stages of A in registers");
+    if (wid < Cfg::WM * Cfg::WN / 2) {  // uniform over a wavefront
+      for (int s = 0; s < steps; s += 2) {
+        pp_step(std::integral_constant<int, 0>{}, s, std::false_type{});
+        pp_step(std::integral_constant<int, 1>{}, s + 1, std::false_type{});
+      }
+    } else {
+      for (int s = 0; s < steps; s += 2) {
+        pp_step(std::integral_constant<int, 0>{}, s, std::true_type{});
+        pp_step(std::integral_constant<int, 1>{}, s + 1, std::true_type{});
+      }
+    }
+  } else if constexpr (PD == 4) {
+    for (int s = 0; s < steps; s += 4) {
+      step(std::integral_constant<int, 0>{}, s);
+      step(std::integral_constant<int, 1>{}, s + 1);
+      step(std::integral_constant<int, 2>{}, s + 2);
+      step(std::integral_constant<int, 3>{}, s + 3);
+    }
+  } else {
+    for (int s = 0; s < steps; s += 2) {
+      step(std::integral_constant<int, 0>{}, s);
+      step(std::integral_constant<int, 1>{}, s + 1);
+    }
   }
 
   // Epilogue. 32x32 accumulator layout: register e of lane l holds row
   // 8*(e/4) + 4*(l/32) + (e%4), column l%32 of the MFMA tile.
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < TN; ++j) {
+      const int64_t gn = n0 + wn * Cfg::kWaveN + j * 32 + (lane & 31);
       if (gn >= n) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int gm = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int gm = m0 + wm * Cfg::kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (gm < m) c[gm * ldc + gn] = bf16_rne(acc[i][j][e]);
       }
     }
   }
+}
+
+template <typename Cfg>
+const void* kernel_ptr(int layout) {
+  return layout == kDual ? reinterpret_cast<const void*>(&gemm_kernel<kDual, Cfg>)
+                         : reinterpret_cast<const void*>(&gemm_kernel<kFast, Cfg>);
+}
+
+// Raises the dynamic-LDS limit of both configurations once per device; threads that
+// race repeat the same idempotent calls.
+hipError_t ensure_attributes(int layout) {
+  static std::atomic<bool> done[64][2];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached && done[dev][layout].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel_ptr<MainCfg>(layout), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          MainCfg::kLdsBytes);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(kernel_ptr<TailCfg>(layout), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          TailCfg::kLdsBytes);
+  if (e != hipSuccess) return e;
+  if (cached) done[dev][layout].store(true, std::memory_order_release);
+  return hipSuccess;
+}
+
+// Columns [n_base, n_end) of C for rows [0, m), tiled with configuration Cfg.
+template <typename Cfg>
+hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint16_t* a, int m,
+                         int64_t lda, uint16_t* c, int64_t ldc, int64_t n_base, int64_t n_end,
+                         hipStream_t stream) {
+  if (n_end <= n_base) return hipSuccess;
+  const int m_tiles = (m + Cfg::BM - 1) / Cfg::BM;
+  // At most 2^39 elements of C (checked by the API): at most 2^26 workgroups.
+  const int64_t n_tiles = (n_end - n_base + Cfg::BN - 1) / Cfg::BN;
+  const dim3 grid(static_cast<unsigned>(m_tiles * n_tiles));
+  if (layout == kDual)
+    gemm_kernel<kDual, Cfg><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>(
+        w, n, nb, a, m, lda, c, ldc, m_tiles, n_base);
+  else
+    gemm_kernel<kFast, Cfg><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>(
+        w, n, nb, a, m, lda, c, ldc, m_tiles, n_base);
+  return hipGetLastError();
+}
+
+// Time of one round of tail pieces relative to one round of main tiles.
+constexpr double kTailRoundCost = 0.22;
+
+// Number of trailing 256-column strips of C computed as tail pieces, minimizing whole
+// rounds of main tiles plus weighted rounds of tail pieces. RFP4_GEMM_PLAN set to
+// "main" or "tail" forces all-main or all-tail (lets tests cover both configurations
+// at small sizes).
+int64_t choose_tail_strips(int64_t m, int64_t n, int cus) {
+  const int64_t strips = (n + MainCfg::BN - 1) / MainCfg::BN;
+  const char* plan = getenv("RFP4_GEMM_PLAN");
+  if (plan != nullptr && strcmp(plan, "main") == 0) return 0;
+  if (plan != nullptr && strcmp(plan, "tail") == 0) return strips;
+  const int64_t mt = (m + MainCfg::BM - 1) / MainCfg::BM;
+  const int64_t slabs = (m + TailCfg::BM - 1) / TailCfg::BM;
+  int64_t best = 0;
+  double best_cost = 1e300;
+  const int64_t max_tail = strips < 256 ? strips : 256;
+  for (int64_t t = 0; t <= max_tail; ++t) {
+    const int64_t main_tiles = mt * (strips - t);
+    const int64_t tail_cols = n - (strips - t) * MainCfg::BN;
+    const int64_t pieces = t > 0 ? slabs * ((tail_cols + TailCfg::BN - 1) / TailCfg::BN) : 0;
+    const double cost = static_cast<double>((main_tiles + cus - 1) / cus) +
+                        kTailRoundCost * static_cast<double>((pieces + cus - 1) / cus);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = t;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -255,36 +739,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
 hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
                        int64_t m, int64_t lda, uint16_t* c, int64_t ldc, hipStream_t stream) {
   const int nb = static_cast<int>(k / 32);
-  const size_t shm = 4 * static_cast<size_t>(kTileBytes);  // 128 KB
-  // The dynamic-LDS limit is raised once per device and layout; threads that race
-  // repeat the same idempotent call.
-  static std::atomic<bool> attr_set[64][2];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  // The kernel runs two 64-column steps per iteration; rows of whole 16-byte multiples
+  // (checked by the API) give k % 256 == 0.
+  if (nb % 4 != 0) return hipErrorInvalidValue;
+  hipError_t e = ensure_attributes(layout);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !attr_set[dev][layout].load(std::memory_order_acquire)) {
-    const void* fn = layout == kDual ? reinterpret_cast<const void*>(&gemm_kernel<kDual>)
-                                     : reinterpret_cast<const void*>(&gemm_kernel<kFast>);
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr_set[dev][layout].store(true, std::memory_order_release);
-  }
-  const int64_t n_tiles = (n + BN - 1) / BN;
-  // Launch in chunks of whole M-tile groups so the grid stays within 2^31 workgroups.
+  const int cus = device_cu_count();
+  const int64_t strips = (n + MainCfg::BN - 1) / MainCfg::BN;
+  // Launch in chunks of rows so each grid stays within 2^31 workgroups.
   const int64_t max_m = int64_t(1) << 20;
   for (int64_t m_off = 0; m_off < m; m_off += max_m) {
-    const int64_t mc = (m - m_off < max_m) ? (m - m_off) : max_m;
-    const int m_tiles = static_cast<int>((mc + BM - 1) / BM);
-    const dim3 grid(static_cast<unsigned>(m_tiles * n_tiles));
+    const int mc = static_cast<int>(m - m_off < max_m ? m - m_off : max_m);
+    const int64_t tail = choose_tail_strips(mc, n, cus);
+    const int64_t n_split = (strips - tail) * MainCfg::BN;
     const uint16_t* ap = a + m_off * lda;
     uint16_t* cp = c + m_off * ldc;
-    if (layout == kDual)
-      gemm_kernel<kDual><<<grid, dim3(kThreads), shm, stream>>>(w, static_cast<int>(n), nb, ap,
-                                                                static_cast<int>(mc), lda, cp, ldc, m_tiles);
-    else
-      gemm_kernel<kFast><<<grid, dim3(kThreads), shm, stream>>>(w, static_cast<int>(n), nb, ap,
-                                                                static_cast<int>(mc), lda, cp, ldc, m_tiles);
-    e = hipGetLastError();
+    e = launch_region<MainCfg>(w, layout, static_cast<int>(n), nb, ap, mc, lda, cp, ldc, 0, n_split,
+                               stream);
+    if (e != hipSuccess) return e;
+    e = launch_region<TailCfg>(w, layout, static_cast<int>(n), nb, ap, mc, lda, cp, ldc, n_split, n,
+                               stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -319,22 +319,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
   }
 }
 
-// CU count of the current device, queried once per device and kept in an atomic
-// cache (threads that race store the same value).
-int device_cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int c = cached[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
 
 struct Plan {
   int p, nu, log2cl, groups, gpw, wgs;
@@ -408,6 +392,23 @@ hipError_t launch2(const uint8_t* w, int n, int nb, const uint16_t* x, int batch
 }
 
 }  // namespace
+
+// CU count of the current device, queried once per device and kept in an atomic
+// cache (threads that race store the same value).
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 hipError_t launch_gemv(const uint8_t* w, int layout, int64_t n, int64_t k, const void* x,
                        int xdtype, int batch, int64_t ldx, float* y, int64_t ldy,

@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = 2147483647;  // n, m, k <= 2^31 - 1
+constexpr int64_t kMaxElems = int64_t(1) << 39;  // elements of A or C (2^40 bytes of bf16)
 
 bool layout_ok(int layout) { return layout == RFP4_DUAL || layout == RFP4_FAST; }
 
@@ -109,6 +110,7 @@ rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const voi
   if (st != RFP4_OK) return st;
   if (m < 1 || m > kMaxDim) return RFP4_ERR_SHAPE;
   if (lda < k || ldc < n || lda > kMaxDim || ldc > kMaxDim) return RFP4_ERR_SHAPE;
+  if (lda > kMaxElems / m || ldc > kMaxElems / m) return RFP4_ERR_SHAPE;
   if (a == nullptr || c == nullptr) return RFP4_ERR_NULL;
   if (!aligned16(a) || !aligned16(c) || (lda % 8) != 0 || (ldc % 8) != 0)
     return RFP4_ERR_UNSUPPORTED;

@@ -33,6 +33,24 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kMagE4m3Lo = 0x44403800u;
 constexpr uint32_t kMagE4m3Hi = 0x52504C48u;
 
+// E4M3 encodings of half the magnitudes: 0, 0.5, 1, 1.5 (low word) and 2, 3, 4, 5
+// (high word). With these codes a weight is the product of its code and the full E4M3
+// value of the scale byte (the decoded scale is half of it).
+constexpr uint32_t kHalfE4m3Lo = 0x3C383000u;
+constexpr uint32_t kHalfE4m3Hi = 0x4A484440u;
+
+// Four E4M3 codes of half-weights (byte i = low nibble of byte i of q).
+__device__ __forceinline__ uint32_t half_codes_low(uint32_t q) {
+  const uint32_t mag = __builtin_amdgcn_perm(kHalfE4m3Hi, kHalfE4m3Lo, q & 0x07070707u);
+  return mag | ((q << 4) & 0x80808080u);
+}
+
+// Four E4M3 codes of half-weights (byte i = high nibble of byte i of q).
+__device__ __forceinline__ uint32_t half_codes_high(uint32_t q) {
+  const uint32_t mag = __builtin_amdgcn_perm(kHalfE4m3Hi, kHalfE4m3Lo, (q >> 4) & 0x07070707u);
+  return mag | (q & 0x80808080u);
+}
+
 // Four E4M3 codes (byte i = weight of the low nibble of byte i of q).
 __device__ __forceinline__ uint32_t codes_low(uint32_t q) {
   const uint32_t mag = __builtin_amdgcn_perm(kMagE4m3Hi, kMagE4m3Lo, q & 0x07070707u);

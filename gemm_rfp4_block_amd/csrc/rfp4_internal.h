@@ -17,6 +17,9 @@ constexpr int kBF16 = 1;
 // Bytes per 32-weight block ("Block Layout": qs[16] then e[2] or e).
 constexpr int block_bytes(int layout) { return layout == kDual ? 18 : 17; }
 
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
 // Launchers. Arguments have been checked by the API layer: shapes in range, rows
 // 16-byte aligned, pointers non-null and aligned as the public header requires.
 hipError_t launch_dequant(const uint8_t* w, int layout, int64_t n, int64_t k, float* out,

@@ -113,7 +113,13 @@ RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, 
  *   c[i * ldc + r] = bf16_rne( sum_q a[i * lda + q] * weight(r, q) ),  i < m, r < n
  * i.e. C = A * W^T with A (m x k, bf16, row-major) and C (m x n, bf16, row-major);
  * weight tiles are decoded to bf16 in LDS and multiplied on the matrix cores with
- * fp32 accumulation. lda >= k (lda % 8 == 0), ldc >= n (ldc % 8 == 0). */
+ * fp32 accumulation. lda >= k (lda % 8 == 0), ldc >= n (ldc % 8 == 0), and
+ * m * lda, m * ldc <= 2^39 (RFP4_ERR_SHAPE otherwise). The columns of C are split
+ * between a launch of 256 x 256 tiles and a launch of 128 x 64 tiles so that the
+ * CUs get balanced work; the environment variable RFP4_GEMM_PLAN, read on each
+ * call, set to "main" or "tail" forces one tile size for the whole matrix (results
+ * are the same either way up to fp32 summation order, which is fixed per tile
+ * size). */
 RFP4_API rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
                       int64_t m, int64_t lda, void* c, int64_t ldc, void* stream);
 

@@ -304,12 +304,42 @@ def test_gemm_same_sign_rounding():
     assert np.all(np.abs(c - ref_bf) <= ulp + 1e-30)
 
 
+@pytest.mark.parametrize("plan", ["main", "tail"])
+@pytest.mark.parametrize("case", [(0, 100, 200, 512), (1, 77, 136, 1024), (0, 257, 520, 2304),
+                                  (1, 300, 264, 512)], ids=lambda c: "L{}m{}n{}k{}".format(*c))
+def test_gemm_forced_tile_size(case, plan, monkeypatch):
+    """Each tile configuration alone over the whole matrix, ragged edges included."""
+    monkeypatch.setenv("RFP4_GEMM_PLAN", plan)
+    layout, m, n, k = case
+    rng = np.random.default_rng(4000 + m + n + k)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    a = synth.activations(rng, m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a, ldc=n + 8)
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c, c_ref, den) <= TOL
+
+
+def test_gemm_mixed_tile_sizes():
+    """2048 x 8448: 256 full tiles plus one strip of 256 columns that the launcher splits
+    into 128 x 64 pieces; every output is compared, across the boundary at column 8192."""
+    layout, m, n, k = 0, 2048, 8448, 256
+    rng = np.random.default_rng(4321)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.01)
+    a = synth.activations(rng, m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a)
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c, c_ref, den) <= TOL
+
+
 def test_gemm_full_size_sampled():
     w, a, cfg = synth.gemm_inputs("prefill")
     n, k, m = cfg["n"], cfg["k"], cfg["m"]
     c = run_gemm(w, cfg["layout"], n, k, a)
     rng = np.random.default_rng(99)
-    cols = np.sort(rng.choice(n, size=96, replace=False))
+    # Random columns plus the edges of the last 256-column strips, where the launcher
+    # may switch tile size.
+    edges = np.array([0, 255, 256, n - 1025, n - 1024, n - 513, n - 512, n - 257, n - 256, n - 65, n - 64, n - 1])
+    cols = np.unique(np.concatenate([rng.choice(n, size=96, replace=False), edges]))
     c_ref, den = O.gemm_rows(w, cfg["layout"], n, k, x64(a), cols)
     assert gemm_error(c[:, cols], c_ref, den) <= TOL
     assert np.all(np.isfinite(c))
