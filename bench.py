@@ -71,6 +71,20 @@ def timed_launches(torch, fn, count):
     return [s.elapsed_time(e) for s, e in ev]
 
 
+def warm_up(torch, fn, seconds=0.3):
+    """Call fn until `seconds` of wall time have passed (synchronizing every few calls),
+    so that the timed region starts with the GPU clocks at their steady level (they
+    take a few hundred milliseconds of load to settle)."""
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def rotation_copies(torch, R, layout, n, k, base_w, dev, seed0):
     import synth
 
@@ -87,6 +101,7 @@ def bench_gemv_graph(torch, R, copies, layout, n, k, x, y, steps, warmup):
     nc = len(copies)
     for i in range(warmup):
         R.rfp4_gemv(copies[i % nc], layout, n, k, x, y)
+    warm_up(torch, lambda i: R.rfp4_gemv(copies[i % nc], layout, n, k, x, y))
     torch.cuda.synchronize()
     eager_ref = R.rfp4_gemv(copies[(steps - 1) % nc], layout, n, k, x).clone()
     g = torch.cuda.CUDAGraph()
@@ -241,9 +256,8 @@ def main():
         wg = torch.from_numpy(wg_host).to(dev)
         a = a_host.to(dev)
         c = torch.empty((gm, gn), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c)
-        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c), 20))
+        warm_up(torch, lambda i: R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c))
+        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c), 50))
         flops = 2.0 * gm * gn * gk
         tf = flops / (d["mean_us"] * 1e-6) / 1e12
         gemm = {"TFLOP/s": round(tf, 1), "flop": flops, "m": gm, "n": gn, "k": gk,

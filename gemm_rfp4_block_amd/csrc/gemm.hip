@@ -36,6 +36,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <string>
 #include <type_traits>
 
 #include "rfp4_decode.h"
@@ -86,7 +88,7 @@ struct TileCfg {
   static_assert(kARows % 16 == 0 && BM % kARows == 0 && kAPasses <= 8, "A loader shape");
   static_assert(kBlocks % kThreads == 0 || kThreads % kBlocks == 0, "decode split");
   static_assert(kDecThreads <= 4 && kBlocksPerThread <= 2, "decode split");
-  static_assert(kAPrefetch == 1 || kAPrefetch == 2 || kAPrefetch == 4, "A prefetch depth");
+  static_assert(kAPrefetch == 1 || kAPrefetch == 2, "A prefetch depth");
   static_assert(kDecThreads == 1 || kBlocks % 64 == 0, "decode group uniform per wavefront");
   static_assert(kWaveM % 16 == 0 && kWaveN % 16 == 0, "fragment rows share a swizzle term");
   // Fragment reads use one base register per k slice and operand, plus an immediate
@@ -113,21 +115,24 @@ using MainCfg = std::conditional_t<
     std::conditional_t<RFP4_GEMM_MAIN == 2, TileCfg<256, 256, 2, 2, RFP4_GEMM_MAIN_PD>,
                        std::conditional_t<RFP4_GEMM_PINGPONG != 0, TileCfg<256, 256, 4, 2, 2, true>,
                                           TileCfg<256, 256, 4, 2, RFP4_GEMM_MAIN_PD>>>>;
-// Tail pieces: 0 = 128 x 64, four wavefronts (64 x 32 each); 1 = 128 x 64, eight
+// Tail tiles: 4 = 128 x 128, eight wavefronts (32 x 64 each) on the ping-pong schedule;
+// 0 = 128 x 64, four wavefronts (64 x 32 each); 1 = 128 x 64, eight
 // wavefronts (32 x 32 each); 2 = 64 x 64, four wavefronts (32 x 32 each); 3 = 128 x 32,
 // four wavefronts (32 x 32 each). RFP4_GEMM_TAIL_PD: steps of A prefetched.
 #ifndef RFP4_GEMM_TAIL
-#define RFP4_GEMM_TAIL 0
+#define RFP4_GEMM_TAIL 4
 #endif
 #ifndef RFP4_GEMM_TAIL_PD
 #define RFP4_GEMM_TAIL_PD 2
 #endif
 using TailCfg = std::conditional_t<
+    RFP4_GEMM_TAIL == 4, TileCfg<128, 128, 4, 2, 2, true>,
+    std::conditional_t<
     RFP4_GEMM_TAIL == 1, TileCfg<128, 64, 4, 2, RFP4_GEMM_TAIL_PD>,
     std::conditional_t<
         RFP4_GEMM_TAIL == 2, TileCfg<64, 64, 2, 2, RFP4_GEMM_TAIL_PD>,
         std::conditional_t<RFP4_GEMM_TAIL == 3, TileCfg<128, 32, 4, 1, RFP4_GEMM_TAIL_PD>,
-                           TileCfg<128, 64, 2, 2, RFP4_GEMM_TAIL_PD>>>>;
+                           TileCfg<128, 64, 2, 2, RFP4_GEMM_TAIL_PD>>>>>;
 
 // LDS tiles are rows of 64 bf16 (128 bytes, eight 16-byte chunks); chunk c of row r
 // is stored at chunk position c ^ ((r >> 1) & 7). A 16-byte access by 16 lanes covers
@@ -261,17 +266,22 @@ __device__ __forceinline__ void decode_part(const BlockRaw& b, const uint4* tabs
   }
 }
 
-// One workgroup computes tile (blockIdx.x mod m_tiles, blockIdx.x / m_tiles) of the
-// region of C whose columns start at n_base; rows and columns outside [0, m) x [0, n)
-// are computed on clamped inputs and never stored. `steps` (= k / 64) must be even.
+// Workgroup b computes tile t = b mod tiles, i.e. (t mod m_tiles, t / m_tiles), of the
+// region of C whose columns start at n_base, over the part b / tiles of `splits`
+// equal, even-length ranges of the k steps (k / 64 of them, an even number, at least
+// 2 * splits). With one split the tile is rounded to bf16 and stored; with more, the
+// fp32 accumulators go to partial[b] (BM x BN floats in accumulator order) for
+// gemm_reduce_kernel. Rows and columns outside [0, m) x [0, n) are computed on clamped
+// inputs and never stored.
 template <int LAYOUT, typename Cfg>
 __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __restrict__ w,
                                                              int n, int nb,
                                                              const uint16_t* __restrict__ a,
                                                              int m, int64_t lda,
                                                              uint16_t* __restrict__ c,
-                                                             int64_t ldc, int m_tiles,
-                                                             int64_t n_base) {
+                                                             int64_t ldc, int m_tiles, int tiles,
+                                                             int64_t n_base, int splits,
+                                                             float* __restrict__ partial) {
   constexpr int BB = block_bytes(LAYOUT);
   constexpr int TM = Cfg::TM;
   constexpr int TN = Cfg::TN;
@@ -285,11 +295,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / Cfg::WN;
   const int wn = wid % Cfg::WN;
-  const int tile_id = blockIdx.x;
+  const int tile_id = static_cast<int>(blockIdx.x) % tiles;
+  const int split = static_cast<int>(blockIdx.x) / tiles;
   const int m0 = (tile_id % m_tiles) * Cfg::BM;
   const int64_t n0 = n_base + static_cast<int64_t>(tile_id / m_tiles) * Cfg::BN;
   const int64_t rowbytes = static_cast<int64_t>(nb) * BB;
-  const int steps = nb / 2;  // BK = 64 = two blocks
+  const int half_steps = nb / 4;  // BK = 64 = two blocks; steps come in pairs
+  const int s_begin = 2 * static_cast<int>(static_cast<int64_t>(split) * half_steps / splits);
+  const int s_end = 2 * static_cast<int>(static_cast<int64_t>(split + 1) * half_steps / splits);
+  const int s_last = s_end - 1;
 
   // A loader: thread -> 16-byte chunk (t % 8) of rows t/8 + kARows * i (eight threads
   // cover a row's 128 contiguous bytes); staged in registers, written to the swizzled
@@ -401,8 +415,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
   // Prologue: stage 0 in LDS, the weights of stage 1 and the A chunks of stages
   // 1 .. PD - 1 in registers.
   {
-    const AChunks a0 = load_a(0);
-    const WRaw b0 = load_w(0);
+    const AChunks a0 = load_a(s_begin);
+    const WRaw b0 = load_w(s_begin);
 #if RFP4_GEMM_LUT
     // Decode table: entry e (the low seven bits of a scale byte) holds bf16(m * S(e))
     // for the magnitudes m = 0, 1, 2, 3, 4, 6, 8, 10 as a low-byte and a high-byte
@@ -428,9 +442,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
     decode_slot(b0, t0, 0, std::integral_constant<int, 2>{});
     decode_slot(b0, t0, 0, std::integral_constant<int, 3>{});
   }
-  WRaw w_next = load_w(min(1, steps - 1));
+  WRaw w_next = load_w(min(s_begin + 1, s_last));
 #pragma unroll
-  for (int p = 1; p < PD; ++p) a_ring[p] = load_a(min(p, steps - 1));
+  for (int p = 1; p < PD; ++p) a_ring[p] = load_a(min(s_begin + p, s_last));
   __syncthreads();
 
   // Fragment addresses. Lane (fr, fk) reads row fr of each 32-row MFMA tile and the
@@ -464,8 +478,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
     // Issue order matters: the A loads first and the weight loads after them, so that
     // storing A at the end of the step waits only for the A loads (vmcnt counts in
     // issue order); the scheduling barrier keeps the compiler from sinking the loads.
-    a_ring[U % PD] = load_a(min(s + PD, steps - 1));
-    const WRaw w_after = load_w(min(s + 2, steps - 1));  // two steps ahead
+    a_ring[U % PD] = load_a(min(s + PD, s_last));
+    const WRaw w_after = load_w(min(s + 2, s_last));  // two steps ahead
     __builtin_amdgcn_sched_barrier(0);
     const WTab tn = load_tabs(w_next);
     bf16x8 af[2][TM], bfr[2][TN];
@@ -581,8 +595,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
   auto prep_block = [&](auto u_c, int s) {
     constexpr int U = decltype(u_c)::value;
     constexpr int cur = U & 1;
-    a_ring[U % PD] = load_a(min(s + PD, steps - 1));
-    const WRaw w_after = load_w(min(s + 2, steps - 1));
+    a_ring[U % PD] = load_a(min(s + PD, s_last));
+    const WRaw w_after = load_w(min(s + 2, s_last));
     __builtin_amdgcn_sched_barrier(0);
     const WTab tn = load_tabs(w_next);
     decode_slot(w_next, tn, cur ^ 1, std::integral_constant<int, 0>{});
@@ -614,29 +628,23 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
     }
   };
 
-  // steps is a multiple of 4 (k % 256 == 0).
+  // The range [s_begin, s_end) has even bounds, so stage s lives in buffer s % 2 and
+  // ring slot s % PD.
   if constexpr (Cfg::kPingPong) {
     static_assert(PD == 2, "the ping-pong schedule keeps two stages of A in registers");
     if (wid < Cfg::WM * Cfg::WN / 2) {  // uniform over a wavefront
-      for (int s = 0; s < steps; s += 2) {
+      for (int s = s_begin; s < s_end; s += 2) {
         pp_step(std::integral_constant<int, 0>{}, s, std::false_type{});
         pp_step(std::integral_constant<int, 1>{}, s + 1, std::false_type{});
       }
     } else {
-      for (int s = 0; s < steps; s += 2) {
+      for (int s = s_begin; s < s_end; s += 2) {
         pp_step(std::integral_constant<int, 0>{}, s, std::true_type{});
         pp_step(std::integral_constant<int, 1>{}, s + 1, std::true_type{});
       }
     }
-  } else if constexpr (PD == 4) {
-    for (int s = 0; s < steps; s += 4) {
-      step(std::integral_constant<int, 0>{}, s);
-      step(std::integral_constant<int, 1>{}, s + 1);
-      step(std::integral_constant<int, 2>{}, s + 2);
-      step(std::integral_constant<int, 3>{}, s + 3);
-    }
   } else {
-    for (int s = 0; s < steps; s += 2) {
+    for (int s = s_begin; s < s_end; s += 2) {
       step(std::integral_constant<int, 0>{}, s);
       step(std::integral_constant<int, 1>{}, s + 1);
     }
@@ -644,6 +652,21 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
 
   // Epilogue. 32x32 accumulator layout: register e of lane l holds row
   // 8*(e/4) + 4*(l/32) + (e%4), column l%32 of the MFMA tile.
+  if (partial != nullptr) {
+    // Partial sums, stored as float4 groups (registers 4 e4 .. 4 e4 + 3) at index
+    // ((wave * TM + i) * TN + j) * 4 + e4 of 64 lanes each: 1 KB contiguous per store.
+    float4* dst = reinterpret_cast<float4*>(partial + static_cast<int64_t>(blockIdx.x) * Cfg::BM * Cfg::BN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          dst[(((wid * TM + i) * TN + j) * 4 + e4) * 64 + lane] =
+              make_float4(acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
+                          acc[i][j][4 * e4 + 3]);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -657,6 +680,49 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
       }
     }
   }
+}
+
+// Sums the `splits` partial tiles of each of `tiles` tiles (split order 0, 1, ...),
+// rounds to bf16 and stores the tile's part of C. Thread g handles float4 group g of
+// the accumulator order written by gemm_kernel.
+template <typename Cfg>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ partial,
+                                                          int splits, int tiles, int m_tiles,
+                                                          int64_t n_base, int m, int n,
+                                                          uint16_t* __restrict__ c, int64_t ldc) {
+  constexpr int kGroups = Cfg::BM * Cfg::BN / 4;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= static_cast<int64_t>(tiles) * kGroups) return;
+  const int tile = static_cast<int>(g / kGroups);
+  const int idx = static_cast<int>(g % kGroups);
+  const float4* p = reinterpret_cast<const float4*>(partial);
+  float4 sum = p[static_cast<int64_t>(tile) * kGroups + idx];
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 v = p[(static_cast<int64_t>(sp) * tiles + tile) * kGroups + idx];
+    sum.x += v.x;
+    sum.y += v.y;
+    sum.z += v.z;
+    sum.w += v.w;
+  }
+  const int lane = idx % 64;
+  int r = idx / 64;
+  const int e4 = r % 4;
+  r /= 4;
+  const int j = r % Cfg::TN;
+  r /= Cfg::TN;
+  const int i = r % Cfg::TM;
+  const int wid = r / Cfg::TM;
+  const int wm = wid / Cfg::WN;
+  const int wn = wid % Cfg::WN;
+  const int m0 = (tile % m_tiles) * Cfg::BM;
+  const int64_t n0 = n_base + static_cast<int64_t>(tile / m_tiles) * Cfg::BN;
+  const int64_t gn = n0 + wn * Cfg::kWaveN + j * 32 + (lane & 31);
+  if (gn >= n) return;
+  const int row0 = m0 + wm * Cfg::kWaveM + i * 32 + 8 * e4 + 4 * (lane >> 5);
+  const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (row0 + q < m) c[(row0 + q) * ldc + gn] = bf16_rne(v[q]);
 }
 
 template <typename Cfg>
@@ -684,54 +750,133 @@ hipError_t ensure_attributes(int layout) {
   return hipSuccess;
 }
 
-// Columns [n_base, n_end) of C for rows [0, m), tiled with configuration Cfg.
+// Columns [n_base, n_end) of C for rows [0, m), tiled with configuration Cfg, each tile's
+// k range split `splits` ways (partial sums in `partial`, then reduced) when splits > 1.
 template <typename Cfg>
 hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint16_t* a, int m,
                          int64_t lda, uint16_t* c, int64_t ldc, int64_t n_base, int64_t n_end,
-                         hipStream_t stream) {
+                         int splits, float* partial, hipStream_t stream) {
   if (n_end <= n_base) return hipSuccess;
   const int m_tiles = (m + Cfg::BM - 1) / Cfg::BM;
-  // At most 2^39 elements of C (checked by the API): at most 2^26 workgroups.
+  // At most 2^39 elements of C (checked by the API): at most 2^26 tiles.
   const int64_t n_tiles = (n_end - n_base + Cfg::BN - 1) / Cfg::BN;
-  const dim3 grid(static_cast<unsigned>(m_tiles * n_tiles));
+  const int tiles = static_cast<int>(m_tiles * n_tiles);
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(tiles) * splits));
+  float* part = splits > 1 ? partial : nullptr;
   if (layout == kDual)
     gemm_kernel<kDual, Cfg><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>(
-        w, n, nb, a, m, lda, c, ldc, m_tiles, n_base);
+        w, n, nb, a, m, lda, c, ldc, m_tiles, tiles, n_base, splits, part);
   else
     gemm_kernel<kFast, Cfg><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>(
-        w, n, nb, a, m, lda, c, ldc, m_tiles, n_base);
+        w, n, nb, a, m, lda, c, ldc, m_tiles, tiles, n_base, splits, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t groups = static_cast<int64_t>(tiles) * (Cfg::BM * Cfg::BN / 4);
+  gemm_reduce_kernel<Cfg><<<dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256), 0, stream>>>(
+      partial, splits, tiles, m_tiles, n_base, m, n, c, ldc);
   return hipGetLastError();
 }
 
-// Time of one round of tail pieces relative to one round of main tiles.
-constexpr double kTailRoundCost = 0.22;
+// Relative times used to choose a plan: one round of 128 x 128 tail tiles (full k) and
+// the reduction of split partial sums, each against one round of main tiles.
+constexpr double kTailRoundCost = 0.35;
+constexpr double kReduceCost = 0.03;
 
-// Number of trailing 256-column strips of C computed as tail pieces, minimizing whole
-// rounds of main tiles plus weighted rounds of tail pieces. RFP4_GEMM_PLAN set to
-// "main" or "tail" forces all-main or all-tail (lets tests cover both configurations
-// at small sizes).
-int64_t choose_tail_strips(int64_t m, int64_t n, int cus) {
+struct Plan {
+  int64_t tail_strips;  // trailing 256-column strips of C computed with tail tiles
+  int splits;           // k-range split of each tail tile
+  int64_t tail_tiles;   // tail tiles (before the split)
+};
+
+// Chooses the tail strips and split that minimize rounds of main tiles plus weighted
+// rounds of tail tiles (per split) plus the reduction. RFP4_GEMM_PLAN = "main", "tail",
+// "tail2" or "tail4" forces all-main tiles or all-tail tiles with that split (lets tests
+// cover every path at small sizes); "nosplit" keeps the choice of strips but no split.
+Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
   const int64_t strips = (n + MainCfg::BN - 1) / MainCfg::BN;
-  const char* plan = getenv("RFP4_GEMM_PLAN");
-  if (plan != nullptr && strcmp(plan, "main") == 0) return 0;
-  if (plan != nullptr && strcmp(plan, "tail") == 0) return strips;
   const int64_t mt = (m + MainCfg::BM - 1) / MainCfg::BM;
   const int64_t slabs = (m + TailCfg::BM - 1) / TailCfg::BM;
-  int64_t best = 0;
+  auto tail_tiles = [&](int64_t t) {
+    const int64_t cols = n - (strips - t) * MainCfg::BN;
+    return t > 0 ? slabs * ((cols + TailCfg::BN - 1) / TailCfg::BN) : 0;
+  };
+  const int max_split = nb / 4;  // each split needs at least two 64-column steps
+  const char* env = getenv("RFP4_GEMM_PLAN");
+  const std::string plan = env != nullptr ? env : "";
+  if (plan == "main") return Plan{0, 1, 0};
+  if (plan == "tail" || plan == "tail2" || plan == "tail4") {
+    int sp = plan == "tail" ? 1 : (plan == "tail2" ? 2 : 4);
+    if (sp > max_split) sp = max_split;
+    return Plan{strips, sp, tail_tiles(strips)};
+  }
+  const bool allow_split = plan != "nosplit";
+  Plan best{0, 1, 0};
   double best_cost = 1e300;
   const int64_t max_tail = strips < 256 ? strips : 256;
   for (int64_t t = 0; t <= max_tail; ++t) {
     const int64_t main_tiles = mt * (strips - t);
-    const int64_t tail_cols = n - (strips - t) * MainCfg::BN;
-    const int64_t pieces = t > 0 ? slabs * ((tail_cols + TailCfg::BN - 1) / TailCfg::BN) : 0;
-    const double cost = static_cast<double>((main_tiles + cus - 1) / cus) +
-                        kTailRoundCost * static_cast<double>((pieces + cus - 1) / cus);
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = t;
+    const int64_t tt = tail_tiles(t);
+    for (int sp = 1; sp <= 8; sp *= 2) {
+      if (sp > 1 && (!allow_split || sp > max_split || tt == 0)) break;
+      const double rounds_main = static_cast<double>((main_tiles + cus - 1) / cus);
+      const double rounds_tail = static_cast<double>((tt * sp + cus - 1) / cus);
+      const double cost = rounds_main + kTailRoundCost * rounds_tail / sp + (sp > 1 ? kReduceCost : 0.0);
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = Plan{t, sp, tt};
+      }
     }
   }
   return best;
+}
+
+// Workspace for split partial sums, one per (device, stream) so that calls ordered on a
+// stream reuse it and calls on different streams never share it. It grows on demand
+// (after the stream's earlier work has finished) and is kept until the process ends.
+hipError_t split_workspace(hipStream_t stream, size_t bytes, float** out) {
+  struct Entry {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+  };
+  static std::mutex mu;
+  static Entry entries[256];
+  static int count = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  Entry* en = nullptr;
+  for (int i = 0; i < count; ++i)
+    if (entries[i].dev == dev && entries[i].stream == stream) en = &entries[i];
+  if (en == nullptr) {
+    if (count == 256) return hipErrorOutOfMemory;
+    en = &entries[count++];
+    *en = Entry{dev, stream, nullptr, 0};
+  }
+  if (en->bytes < bytes) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    if (en->ptr != nullptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return e;
+      e = hipFree(en->ptr);
+      en->ptr = nullptr;
+      en->bytes = 0;
+      if (e != hipSuccess) return e;
+    }
+    e = hipMalloc(&en->ptr, bytes);
+    if (e != hipSuccess) {
+      en->ptr = nullptr;
+      return e;
+    }
+    en->bytes = bytes;
+  }
+  *out = static_cast<float*>(en->ptr);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -750,15 +895,25 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
   const int64_t max_m = int64_t(1) << 20;
   for (int64_t m_off = 0; m_off < m; m_off += max_m) {
     const int mc = static_cast<int>(m - m_off < max_m ? m - m_off : max_m);
-    const int64_t tail = choose_tail_strips(mc, n, cus);
-    const int64_t n_split = (strips - tail) * MainCfg::BN;
+    Plan plan = choose_plan(mc, n, nb, cus);
+    float* partial = nullptr;
+    if (plan.splits > 1) {
+      const size_t bytes = static_cast<size_t>(plan.tail_tiles) * plan.splits * TailCfg::BM *
+                           TailCfg::BN * sizeof(float);
+      if (split_workspace(stream, bytes, &partial) != hipSuccess) {
+        (void)hipGetLastError();  // clear a failed allocation; run the tail unsplit
+        plan.splits = 1;
+        partial = nullptr;
+      }
+    }
+    const int64_t n_split = (strips - plan.tail_strips) * MainCfg::BN;
     const uint16_t* ap = a + m_off * lda;
     uint16_t* cp = c + m_off * ldc;
     e = launch_region<MainCfg>(w, layout, static_cast<int>(n), nb, ap, mc, lda, cp, ldc, 0, n_split,
-                               stream);
+                               1, nullptr, stream);
     if (e != hipSuccess) return e;
     e = launch_region<TailCfg>(w, layout, static_cast<int>(n), nb, ap, mc, lda, cp, ldc, n_split, n,
-                               stream);
+                               plan.splits, partial, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

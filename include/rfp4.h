@@ -23,9 +23,11 @@
  *
  * General rules for every entry point:
  *   - All pointers except rfp4_validate's `w_host` are device pointers. The caller
- *     owns every buffer; the library never allocates, frees or synchronizes. Its
- *     only global state is a per-device cache of the CU count and of one kernel
- *     attribute, kept in atomics, so calls from several threads are safe.
+ *     owns every buffer it passes. rfp4_dequant and rfp4_gemv never allocate, free
+ *     or synchronize; rfp4_gemm may use a workspace of its own (see there). Global
+ *     state: per-device caches of the CU count and of kernel attributes (atomics)
+ *     and rfp4_gemm's workspaces (behind a mutex), so calls from several threads
+ *     are safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are
  *     asynchronous and ordered on that stream; a fault in a kernel surfaces at the
  *     caller's next synchronization.
@@ -114,12 +116,18 @@ RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, 
  * i.e. C = A * W^T with A (m x k, bf16, row-major) and C (m x n, bf16, row-major);
  * weight tiles are decoded to bf16 in LDS and multiplied on the matrix cores with
  * fp32 accumulation. lda >= k (lda % 8 == 0), ldc >= n (ldc % 8 == 0), and
- * m * lda, m * ldc <= 2^39 (RFP4_ERR_SHAPE otherwise). The columns of C are split
- * between a launch of 256 x 256 tiles and a launch of 128 x 64 tiles so that the
- * CUs get balanced work; the environment variable RFP4_GEMM_PLAN, read on each
- * call, set to "main" or "tail" forces one tile size for the whole matrix (results
- * are the same either way up to fp32 summation order, which is fixed per tile
- * size). */
+ * m * lda, m * ldc <= 2^39 (RFP4_ERR_SHAPE otherwise).
+ * Balance: the columns of C are split between 256 x 256 tiles and trailing strips of
+ * 128 x 128 tiles whose k range may be split in two or more parts, so that the CUs
+ * get equal work. Split tiles write fp32 partial sums to a device workspace that the
+ * library allocates per (device, stream) on first need, grows when a larger one is
+ * needed (synchronizing that stream first) and keeps until the process ends; a
+ * final kernel adds the parts in a fixed order and rounds to bf16. The workspace is
+ * never allocated while the stream is being captured into a graph (the split is
+ * then skipped), so call once before capturing. Results are deterministic for a
+ * given shape and CU count. The environment variable RFP4_GEMM_PLAN, read on each
+ * call, forces a plan: "main" (256 x 256 tiles only), "tail", "tail2", "tail4"
+ * (128 x 128 tiles only, k unsplit or split 2 or 4 ways), "nosplit". */
 RFP4_API rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
                       int64_t m, int64_t lda, void* c, int64_t ldc, void* stream);
 

@@ -304,7 +304,7 @@ def test_gemm_same_sign_rounding():
     assert np.all(np.abs(c - ref_bf) <= ulp + 1e-30)
 
 
-@pytest.mark.parametrize("plan", ["main", "tail"])
+@pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4"])
 @pytest.mark.parametrize("case", [(0, 100, 200, 512), (1, 77, 136, 1024), (0, 257, 520, 2304),
                                   (1, 300, 264, 512)], ids=lambda c: "L{}m{}n{}k{}".format(*c))
 def test_gemm_forced_tile_size(case, plan, monkeypatch):
@@ -320,8 +320,9 @@ def test_gemm_forced_tile_size(case, plan, monkeypatch):
 
 
 def test_gemm_mixed_tile_sizes():
-    """2048 x 8448: 256 full tiles plus one strip of 256 columns that the launcher splits
-    into 128 x 64 pieces; every output is compared, across the boundary at column 8192."""
+    """2048 x 8448: 256 full tiles plus one strip of 256 columns that the launcher computes
+    as 128 x 128 tiles with the k range split in two (partial sums, then a reduction);
+    every output is compared, across the boundary at column 8192."""
     layout, m, n, k = 0, 2048, 8448, 256
     rng = np.random.default_rng(4321)
     w = synth.weights(rng, layout, n, k, stress_frac=0.01)
