@@ -14,11 +14,13 @@
 // 18 (dual) or 17 (fast); its index bytes are realigned with v_alignbyte_b32. The
 // launcher uses pairs unless that leaves too few wavefronts for the shape.
 //
-// Work mapping. A wavefront covers RL rows x CL lanes (RL * CL = 64, CL = gcd(64,
-// units per row)); lane c of a row owns units c, c + CL, c + 2 CL, ... of that row, so
-// each load instruction reads runs of CL * 36 (or 34, 18, 17) contiguous bytes. Every
-// wavefront owns `gpw` consecutive row groups and all wavefronts are resident at
-// once, so the work is evenly split. Each lane keeps three units in flight.
+// Work mapping. A wavefront covers RL rows x CL lanes (RL * CL = 64); lane c of a row
+// owns units c, c + CL, c + 2 CL, ... of that row (the remainder masked when CL does
+// not divide the units of a row), so each load instruction reads runs of CL * 36 (or
+// 34, 18, 17) contiguous bytes. The grid is a whole number r of workgroups per CU, all
+// resident (the LDS request pins r), and workgroup w owns an equal contiguous share of
+// the row groups, which its wavefronts take round-robin: every CU gets the same work.
+// Each lane keeps three units in flight.
 //
 // Arithmetic. Each block's 32 weights are decoded to f16/bf16 pairs (rfp4_decode.h)
 // and multiplied with the activations with v_dot2_f32_{f16,bf16}: one fp32 partial
@@ -30,14 +32,21 @@
 // at xs_index); otherwise they are read from global memory, where they stay
 // cache-resident.
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "rfp4_decode.h"
 #include "rfp4_internal.h"
 
 namespace rfp4 {
 namespace {
 
-constexpr int kThreads = 256;
+// Workgroups of 256 threads, or 1024 when long activation rows are staged in LDS (the
+// staging is then shared by 16 wavefronts and two workgroups fit a CU).
+constexpr int kThreadsSmall = 256;
+constexpr int kThreadsLarge = 1024;
 constexpr int kXLdsBudget = 40 * 1024;
+constexpr int kXLdsBudgetLarge = 80 * 1024;
 
 // Tuning knob (no effect on results): resident wavefronts per CU the launch is sized for.
 #ifndef RFP4_GEMV_WAVES_PER_CU
@@ -73,8 +82,42 @@ struct UnitRaw {
   uint32_t d[P == 1 ? 5 : 9];
 };
 
+// Units whose size is not a multiple of 4 bytes (single blocks; pairs of 17-byte
+// blocks) start at 1-, 2- or 3-byte offsets. Such a unit is read with dword-aligned
+// loads from the word boundary below it and shifted into place per lane with
+// v_alignbyte_b32: unaligned 16-byte loads cost the memory pipeline measurably more.
+// The extra bytes read lie inside the row: rows hold a multiple of 8 (dual) or 16
+// (fast) blocks, so the last unit of a row ends on a word boundary.
+template <int LAYOUT, int P>
+__device__ __forceinline__ void load_unit_realigned(const uint8_t* p, UnitRaw<P>& u) {
+  constexpr int NW = P == 1 ? 5 : 9;  // words covering the unit from its word boundary
+  const int sh = static_cast<int>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(p - sh);
+  uint32_t wv[NW];
+  const uint4 v0 = *reinterpret_cast<const uint4*>(a);
+  wv[0] = v0.x;
+  wv[1] = v0.y;
+  wv[2] = v0.z;
+  wv[3] = v0.w;
+  if constexpr (P == 2) {
+    const uint4 v1 = *reinterpret_cast<const uint4*>(a + 4);
+    wv[4] = v1.x;
+    wv[5] = v1.y;
+    wv[6] = v1.z;
+    wv[7] = v1.w;
+  }
+  wv[NW - 1] = a[NW - 1];
+#pragma unroll
+  for (int i = 0; i < NW - 1; ++i) u.d[i] = __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], sh);
+  u.d[NW - 1] = wv[NW - 1] >> (8 * sh);
+}
+
 template <int LAYOUT, int P>
 __device__ __forceinline__ void load_unit(const uint8_t* p, UnitRaw<P>& u) {
+  if constexpr ((P * block_bytes(LAYOUT)) % 4 != 0 || P == 1) {
+    load_unit_realigned<LAYOUT, P>(p, u);
+    return;
+  }
   const uint4 v0 = load16(p);
   u.d[0] = v0.x;
   u.d[1] = v0.y;
@@ -190,9 +233,14 @@ __device__ __forceinline__ int xs_index(int b, int ud, int nu, int B, int cc) {
 // LDS unit (ud * (4P+1)) when XLDS, else the global address of block P*ud.
 template <int LAYOUT, int XT, int BATCH, bool XLDS, int P, int B>
 __device__ __forceinline__ void unit_block(const UnitRaw<P>& u, const uint4* xu, int xrow,
-                                           const uint16_t* xg, int64_t ldx, float (&acc)[BATCH]) {
+                                           const uint16_t* xg, int64_t ldx, bool valid,
+                                           float (&acc)[BATCH]) {
   float s0, s1;
   unit_scales<LAYOUT, P, B>(u, s0, s1);
+  // A lane past the end of a ragged row re-reads the row's last unit; a zero scale
+  // makes its contribution vanish.
+  s0 = valid ? s0 : 0.f;
+  s1 = valid ? s1 : 0.f;
   auto xunit = [&](int b, int cc) -> uint4 {
     if constexpr (XLDS)
       return xu[b * xrow + 4 * B + cc];
@@ -202,9 +250,9 @@ __device__ __forceinline__ void unit_block(const UnitRaw<P>& u, const uint4* xu,
   block_dot<XT, BATCH>(unit_qs<LAYOUT, P, B>(u), s0, s1, xunit, acc);
 }
 
-template <int LAYOUT, int XT, int BATCH, bool XLDS, int P>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restrict__ w, int n,
-                                                        int nu, int log2cl, int groups, int gpw,
+template <int LAYOUT, int XT, int BATCH, bool XLDS, int P, bool RAGGED, int THREADS>
+__global__ __launch_bounds__(THREADS) void gemv_kernel(const uint8_t* __restrict__ w, int n,
+                                                        int nu, int log2cl, int groups,
                                                         const uint16_t* __restrict__ x,
                                                         int64_t ldx, float* __restrict__ y,
                                                         int64_t ldy) {
@@ -216,13 +264,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
   const int rl = 64 >> log2cl;
   const int r_in = lane >> log2cl;
   const int c = lane & (cl - 1);
-  const int iters = nu >> log2cl;  // units per lane per row
+  // Units per lane per row. When CL does not divide the units of a row (RAGGED), the
+  // last iteration covers the remainder and the lanes past the end are masked.
+  const int iters = RAGGED ? (nu + cl - 1) >> log2cl : nu >> log2cl;
   // readfirstlane tells the compiler the wavefront index is uniform, so every cursor
   // and loop bound derived from it lives in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
-  const int g_begin = wave * gpw;
-  const int g_end = min(g_begin + gpw, groups);
-  const int total = g_end > g_begin ? (g_end - g_begin) * iters : 0;  // units per lane
+  // Workgroup w owns the row groups [G w / WGs, G (w + 1) / WGs): the grid is a whole
+  // number of workgroups per CU, all resident, so every CU gets the same share (to one
+  // group). Its wavefronts take the groups round-robin.
+  constexpr int S = THREADS / 64;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g0 = static_cast<int>(static_cast<int64_t>(groups) * blockIdx.x / gridDim.x);
+  const int g1 = static_cast<int>(static_cast<int64_t>(groups) * (blockIdx.x + 1) / gridDim.x);
+  const int g_begin = g0 + wv;
+  const int my_groups = g1 > g_begin ? (g1 - g_begin + S - 1) / S : 0;
+  const int total = my_groups * iters;  // units per lane
   const int64_t rowbytes = static_cast<int64_t>(nu) * UB;  // < 2^31 / 64 (checked by the launcher)
 
   // Load cursor over (row group, unit index); wave-uniform. The address of the next
@@ -233,20 +289,23 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
   const int64_t group_stride = static_cast<int64_t>(rl) * rowbytes;
   const int unit_stride = cl * UB;
   const uint8_t* gbase = w + static_cast<int64_t>(g_begin) * group_stride;
-  int lane_off = min(r_in, max(n - 1 - g_begin * rl, 0)) * static_cast<int>(rowbytes) + c * UB;
+  const int c_off = c * UB;
+  const int last_off = (nu - 1) * UB;
+  int lane_off = min(r_in, max(n - 1 - g_begin * rl, 0)) * static_cast<int>(rowbytes);
   int unit_off = 0;
   int lg = g_begin;
   auto load_next = [&](UnitRaw<P>& buf) {
     if (issued < total) {
-      load_unit<LAYOUT, P>(gbase + unit_off + lane_off, buf);
+      const int col = RAGGED ? min(unit_off + c_off, last_off) : unit_off + c_off;
+      load_unit<LAYOUT, P>(gbase + col + lane_off, buf);
       ++issued;
       unit_off += unit_stride;
       if (++li == iters) {
         li = 0;
         unit_off = 0;
-        ++lg;
-        gbase += group_stride;
-        lane_off = min(r_in, max(n - 1 - lg * rl, 0)) * static_cast<int>(rowbytes) + c * UB;
+        lg += S;
+        gbase += S * group_stride;
+        lane_off = min(r_in, max(n - 1 - lg * rl, 0)) * static_cast<int>(rowbytes);
       }
     }
   };
@@ -260,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
 
   if constexpr (XLDS) {
     const int units = BATCH * 4 * nu * P;  // 16-byte activation units
-    for (int t = threadIdx.x; t < units; t += kThreads) {
+    for (int t = threadIdx.x; t < units; t += THREADS) {
       const int cc = t & 3;
       const int jb = t >> 2;  // block index over all activation rows
       const int b = jb / (nu * P);
@@ -284,11 +343,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
   const uint16_t* xg0 = x + 32 * P * c;
   auto consume = [&](const UnitRaw<P>& u) {
     const int row = cg * rl + r_in;
-    const uint4* xu = xu0 + ci * (cl * (4 * P + 1));
-    const uint16_t* xg = xg0 + ci * (32 * P * cl);
+    const int uidx = c + ci * cl;  // unit of the row this lane holds
+    const bool valid = !RAGGED || uidx < nu;
+    const int ux = RAGGED ? min(uidx, nu - 1) : uidx;
+    const uint4* xu = RAGGED ? xs + ux * (4 * P + 1) : xu0 + ci * (cl * (4 * P + 1));
+    const uint16_t* xg = RAGGED ? x + 32 * P * ux : xg0 + ci * (32 * P * cl);
     // Rows past n were loaded from a clamped address; their sums are never stored.
-    unit_block<LAYOUT, XT, BATCH, XLDS, P, 0>(u, xu, xrow, xg, ldx, acc);
-    if constexpr (P == 2) unit_block<LAYOUT, XT, BATCH, XLDS, P, 1>(u, xu, xrow, xg, ldx, acc);
+    unit_block<LAYOUT, XT, BATCH, XLDS, P, 0>(u, xu, xrow, xg, ldx, valid, acc);
+    if constexpr (P == 2) unit_block<LAYOUT, XT, BATCH, XLDS, P, 1>(u, xu, xrow, xg, ldx, valid, acc);
     if (++ci == iters) {  // row group complete: reduce over the CL lanes of each row
       for (int off = cl >> 1; off >= 1; off >>= 1) {
 #pragma unroll
@@ -301,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) acc[b] = 0.f;
       ci = 0;
-      ++cg;
+      cg += S;
     }
   };
 
@@ -321,25 +383,89 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restric
 
 
 struct Plan {
-  int p, nu, log2cl, groups, gpw, wgs;
+  int p, nu, log2cl, groups, wgs, threads, waves;
+  bool ragged;
 };
 
-// Work plan for P consecutive blocks per lane unit.
-inline Plan make_plan(int p, int n, int nb, int waves_per_cu) {
+// Work plan for P consecutive blocks per lane unit and CL = 2^log2cl lanes per row:
+// `waves` = wavefronts that get at least one row group when the grid is wgs =
+// CUs * (waves_per_cu / waves per workgroup) workgroups.
+inline Plan make_plan(int p, int log2cl, int n, int nb, int waves_per_cu, int threads) {
   Plan pl;
   pl.p = p;
   pl.nu = nb / p;
-  int g = 64;
-  while (pl.nu % g) g >>= 1;  // CL = gcd(64, units per row)
-  pl.log2cl = 0;
-  while ((1 << pl.log2cl) < g) ++pl.log2cl;
-  const int rl = 64 >> pl.log2cl;
+  pl.log2cl = log2cl;
+  pl.threads = threads;
+  const int cl = 1 << log2cl;
+  pl.ragged = (pl.nu % cl) != 0;
+  const int rl = 64 >> log2cl;
   pl.groups = (n + rl - 1) / rl;
-  const int max_waves = device_cu_count() * waves_per_cu;
-  pl.gpw = (pl.groups + max_waves - 1) / max_waves;  // row groups per wavefront
-  const int waves = (pl.groups + pl.gpw - 1) / pl.gpw;
-  pl.wgs = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  // r workgroups per CU: as many as the row groups fill (every wavefront busy), at most
+  // what the occupancy target allows.
+  const int per_wg = threads / 64;
+  const int cus = device_cu_count();
+  const int r_max = waves_per_cu / per_wg > 0 ? waves_per_cu / per_wg : 1;
+  const int64_t slots = static_cast<int64_t>(cus) * per_wg;
+  int r = static_cast<int>((pl.groups + slots - 1) / slots);
+  r = r < 1 ? 1 : (r > r_max ? r_max : r);
+  pl.wgs = cus * r;
+  pl.waves = pl.groups < pl.wgs * per_wg ? pl.groups : pl.wgs * per_wg;
   return pl;
+}
+
+// Lane mapping, from a sweep of all mappings on the decode shapes (17408 x 5120,
+// 6144 x 5120, 1024 x 5120, 5120 x 6144, 5120 x 17408): with the activations in LDS,
+// pairs of blocks per unit (fewer load instructions) and the fewest lanes per row that
+// still give >= 8 resident wavefronts per CU (CL = gcd(64, units per row) or more,
+// with the remainder masked); with activations read from global memory (long rows),
+// single blocks and 64 lanes per row. RFP4_GEMV_PLAN = "P:CL" (P in {1, 2}, CL a power
+// of two up to 64) forces a mapping.
+inline Plan choose_plan(int n, int nb, int waves_per_cu, bool xlds, int threads) {
+  const char* env = getenv("RFP4_GEMV_PLAN");
+  if (env != nullptr) {
+    int fp = 0, fcl = 0;
+    if (sscanf(env, "%d:%d", &fp, &fcl) == 2 && (fp == 1 || (fp == 2 && nb % 2 == 0)) && fcl >= 1 &&
+        fcl <= 64 && (fcl & (fcl - 1)) == 0) {
+      int l = 0;
+      while ((1 << l) < fcl) ++l;
+      return make_plan(fp, l, n, nb, waves_per_cu, threads);
+    }
+  }
+  const int p = (xlds && nb % 2 == 0) ? 2 : 1;
+  if (!xlds) return make_plan(1, 6, n, nb, waves_per_cu, threads);
+  const int nu = nb / p;
+  int g = 64;
+  while (nu % g) g >>= 1;  // gcd(64, nu)
+  int l = 0;
+  while ((1 << l) < g) ++l;
+  const int want = 8 * device_cu_count();
+  Plan pl = make_plan(p, l, n, nb, waves_per_cu, threads);
+  while (l < 6 && pl.waves < want) {
+    ++l;
+    pl = make_plan(p, l, n, nb, waves_per_cu, threads);
+  }
+  return pl;
+}
+
+// The 1024-thread kernels may need more than 64 KB of dynamic LDS; the limit is raised
+// once per process for each (P, ragged) instantiation (an idempotent call, so threads
+// that race repeat it harmlessly).
+template <int LAYOUT, int XT, int BATCH>
+hipError_t raise_lds_limit(int bytes, int p) {
+  static std::atomic<int> done[2];
+  std::atomic<int>& d = done[p - 1];
+  if (d.load(std::memory_order_acquire) >= bytes) return hipSuccess;
+  const void* fns[2] = {
+      reinterpret_cast<const void*>(p == 2 ? &gemv_kernel<LAYOUT, XT, BATCH, true, 2, false, kThreadsLarge>
+                                           : &gemv_kernel<LAYOUT, XT, BATCH, true, 1, false, kThreadsLarge>),
+      reinterpret_cast<const void*>(p == 2 ? &gemv_kernel<LAYOUT, XT, BATCH, true, 2, true, kThreadsLarge>
+                                           : &gemv_kernel<LAYOUT, XT, BATCH, true, 1, true, kThreadsLarge>)};
+  for (const void* f : fns) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+  }
+  d.store(160 * 1024, std::memory_order_release);
+  return hipSuccess;
 }
 
 template <int LAYOUT, int XT, int BATCH>
@@ -348,30 +474,56 @@ hipError_t launch3(const uint8_t* w, int n, int nb, const uint16_t* x, int64_t l
   // Activation bytes in LDS (largest unit size: 4P+1 units of 16 bytes per P blocks).
   const size_t xbytes1 = static_cast<size_t>(BATCH) * nb * 5 * 16;
   const size_t xbytes2 = static_cast<size_t>(BATCH) * (nb / 2) * 9 * 16;
-  const bool xlds = xbytes1 <= static_cast<size_t>(kXLdsBudget);
-  // Resident wavefronts per CU: the knob, capped by what LDS allows (160 KB per CU).
-  int waves_per_cu = RFP4_GEMV_WAVES_PER_CU;
+  const bool small_x = xbytes1 <= static_cast<size_t>(kXLdsBudget);
+  const bool large_x = !small_x && xbytes1 <= static_cast<size_t>(kXLdsBudgetLarge);
+  const bool xlds = small_x || large_x;
+  const int threads = large_x ? kThreadsLarge : kThreadsSmall;
+  // Resident wavefronts per CU: the knob (two whole 16-wavefront workgroups for long
+  // rows), capped by what LDS allows (160 KB per CU).
+  int waves_per_cu = large_x ? 2 * (kThreadsLarge / 64) : RFP4_GEMV_WAVES_PER_CU;
   if (xlds) {
     const int wg_fit = static_cast<int>((160 * 1024) / xbytes1);
-    if (wg_fit * (kThreads / 64) < waves_per_cu) waves_per_cu = wg_fit * (kThreads / 64);
+    if (wg_fit * (threads / 64) < waves_per_cu) waves_per_cu = wg_fit * (threads / 64);
   }
-  // Pairs of blocks halve the per-block load instructions for the scale bytes; use them
-  // unless that leaves too few wavefronts to keep the CUs busy.
-  const Plan p2 = make_plan(2, n, nb, waves_per_cu);
-  const Plan p1 = make_plan(1, n, nb, waves_per_cu);
-  const int min_wgs = device_cu_count() * 3;  // >= 12 resident wavefronts per CU
-  const Plan pl = (p2.wgs >= min_wgs || p2.wgs >= p1.wgs) ? p2 : p1;
-  const dim3 grid(pl.wgs), block(kThreads);
-  const size_t shm = xlds ? (pl.p == 2 ? xbytes2 : xbytes1) : 0;
-#define RFP4_GEMV_LAUNCH(XL, PP)                                                               \
-  gemv_kernel<LAYOUT, XT, BATCH, XL, PP><<<grid, block, shm, stream>>>(w, n, pl.nu, pl.log2cl, \
-                                                                        pl.groups, pl.gpw, x, \
-                                                                        ldx, y, ldy)
-  if (xlds) {
-    if (pl.p == 2) RFP4_GEMV_LAUNCH(true, 2); else RFP4_GEMV_LAUNCH(true, 1);
+  const Plan pl = choose_plan(n, nb, waves_per_cu, xlds, threads);
+  const dim3 grid(pl.wgs), block(pl.threads);
+  // Dynamic LDS: the staged activations, raised to just over 1 / (r + 1) of the CU's
+  // 160 KB so that exactly r = wgs / CUs workgroups are resident per CU (the even split
+  // of row groups relies on it).
+  const int r = pl.wgs / device_cu_count();
+  const size_t pin = (160 * 1024) / (r + 1) + 1024;
+  size_t shm = xlds ? (pl.p == 2 ? xbytes2 : xbytes1) : 0;
+  if (shm < pin) shm = pin;
+  if (shm > 64 * 1024) {
+    const hipError_t e = raise_lds_limit<LAYOUT, XT, BATCH>(static_cast<int>(shm), pl.p);
+    if (e != hipSuccess) return e;
+  }
+#define RFP4_GEMV_LAUNCH(XL, PP, RG, TH)                                                        \
+  gemv_kernel<LAYOUT, XT, BATCH, XL, PP, RG, TH><<<grid, block, shm, stream>>>(                  \
+      w, n, pl.nu, pl.log2cl, pl.groups, x, ldx, y, ldy)
+#define RFP4_GEMV_LAUNCH_P(XL, RG, TH) \
+  if (pl.p == 2) RFP4_GEMV_LAUNCH(XL, 2, RG, TH); else RFP4_GEMV_LAUNCH(XL, 1, RG, TH)
+  if (large_x) {
+    if (pl.ragged) { RFP4_GEMV_LAUNCH_P(true, true, kThreadsLarge); } else { RFP4_GEMV_LAUNCH_P(true, false, kThreadsLarge); }
+  } else if (xlds) {
+    if (pl.ragged) { RFP4_GEMV_LAUNCH_P(true, true, kThreadsSmall); } else { RFP4_GEMV_LAUNCH_P(true, false, kThreadsSmall); }
   } else {
-    if (pl.p == 2) RFP4_GEMV_LAUNCH(false, 2); else RFP4_GEMV_LAUNCH(false, 1);
+    // Activations from global memory: single blocks per unit (a forced P = 2 mapping
+    // keeps its lane count).
+    if (pl.ragged || pl.p == 2) {
+      const Plan p1 = make_plan(1, pl.log2cl, n, nb, waves_per_cu, kThreadsSmall);
+      const dim3 grid1(p1.wgs);
+      if (p1.ragged)
+        gemv_kernel<LAYOUT, XT, BATCH, false, 1, true, kThreadsSmall><<<grid1, block, shm, stream>>>(
+            w, n, p1.nu, p1.log2cl, p1.groups, x, ldx, y, ldy);
+      else
+        gemv_kernel<LAYOUT, XT, BATCH, false, 1, false, kThreadsSmall><<<grid1, block, shm, stream>>>(
+            w, n, p1.nu, p1.log2cl, p1.groups, x, ldx, y, ldy);
+    } else {
+      RFP4_GEMV_LAUNCH(false, 1, false, kThreadsSmall);
+    }
   }
+#undef RFP4_GEMV_LAUNCH_P
 #undef RFP4_GEMV_LAUNCH
   return hipGetLastError();
 }

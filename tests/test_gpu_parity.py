@@ -157,6 +157,26 @@ def test_gemv_ragged(case):
     check_gemv(w, layout, n, k, x, ldx=ldx, ldy=ldy)
 
 
+# Forced lane mappings "P:CL": P blocks per lane unit, CL lanes per row. Cases where CL
+# does not divide the units of a row exercise the masked remainder; the activations are
+# staged in LDS for the small shapes and read from global memory for the long rows.
+GEMV_PLANS = [
+    ("1:64", 0, 75, 2304, 1, "f16"), ("2:64", 0, 75, 2304, 3, "bf16"), ("2:32", 1, 33, 1536, 2, "f16"),
+    ("1:16", 1, 19, 1536, 1, "bf16"), ("2:8", 0, 130, 768, 8, "f16"), ("1:64", 1, 40, 17408, 1, "bf16"),
+    ("2:64", 1, 40, 17408, 2, "bf16"), ("1:32", 0, 9, 256, 1, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", GEMV_PLANS, ids=lambda c: "{}-L{}n{}k{}b{}{}".format(*c))
+def test_gemv_forced_plan(case, monkeypatch):
+    plan, layout, n, k, batch, dt = case
+    monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
+    rng = np.random.default_rng(5000 + n + k + batch)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    x = synth.activations(rng, batch, k, dt)
+    check_gemv(w, layout, n, k, x, ldy=n + 3)
+
+
 def test_gemv_zero_scales_give_zero():
     rng = np.random.default_rng(31)
     n, k = 64, 1024
