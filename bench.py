@@ -36,7 +36,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATE_MIN_BYTES = 600 * 2**20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_up.json")
-GEMV_SOURCES = ["gemm_rfp4_block_amd/csrc/gemv.hip", "gemm_rfp4_block_amd/csrc/rfp4_decode.h"]
+GEMV_SOURCES = ["gemm_rfp4_block_amd/csrc/gemv_impl.h", "gemm_rfp4_block_amd/csrc/gemv_f16.hip",
+                "gemm_rfp4_block_amd/csrc/gemv.hip", "gemm_rfp4_block_amd/csrc/rfp4_decode.h"]
 
 
 def log(*a):
@@ -268,7 +269,33 @@ def main():
         del wg, a, c
         torch.cuda.empty_cache()
 
-    # ---------------- 64-layer decode sweep (448 dual GEMVs, fresh fp16 x per GEMV)
+    # ---------------- fused multi-matrix GEMVs (gate + up, q + k + v), one launch each
+    fused = {}
+    for fname, parts in (("gate_up", [17408, 17408]), ("qkv", [6144, 1024, 1024])):
+        fk = 5120
+        sets = []
+        total_w = sum(n * synth.row_bytes(0, fk) for n in parts)
+        for ci in range(max(2, -(-ROTATE_MIN_BYTES // total_w))):
+            sets.append([synth.weights_device(0, n, fk, 300 + 10 * ci + j, dev) for j, n in enumerate(parts)])
+        xf = synth.activations_device(1, fk, "f16", 301, dev)
+        yfs = [torch.empty((1, n), dtype=torch.float32, device=dev) for n in parts]
+        call_f = lambda i: R.rfp4_gemv_multi(sets[i % len(sets)], 0, parts, fk, xf, yfs)
+        call_s = lambda i: [R.rfp4_gemv(w, 0, n, fk, xf, y) for w, n, y in zip(sets[i % len(sets)], parts, yfs)]
+        warm_up(torch, call_f, 0.1)
+        df = stats_us(timed_launches(torch, call_f, 100))
+        ds = stats_us(timed_launches(torch, call_s, 100))
+        bts = total_w + fk * 2 + sum(parts) * 4
+        fused[fname] = {"parts": parts, "bytes": bts,
+                        "fused_GB/s": round(bts / (df["mean_us"] * 1e-6) / 1e9, 1), "fused_mean_us": round(df["mean_us"], 2),
+                        "separate_GB/s": round(bts / (ds["mean_us"] * 1e-6) / 1e9, 1), "separate_mean_us": round(ds["mean_us"], 2)}
+        log(f"gemv {fname}: fused {df['mean_us']:.2f} us -> {fused[fname]['fused_GB/s']:.0f} GB/s; "
+            f"separate {ds['mean_us']:.2f} us -> {fused[fname]['separate_GB/s']:.0f} GB/s")
+        del sets
+        torch.cuda.empty_cache()
+    extra["gemv_multi"] = fused
+
+    # ---------------- 64-layer decode sweep (448 dual GEMVs): separate launches with a
+    # fresh fp16 x per GEMV, and fused launches (q+k+v and gate+up share their x)
     if not args.no_sweep:
         mats, xs, ys, total = [], [], [], 0
         for layer in range(synth.SWEEP_LAYERS):
@@ -306,7 +333,47 @@ def main():
                                     "ms_per_sweep": round(sweep_ms, 3), "launches": len(mats),
                                     "tokens_per_s_equivalent": round(1e3 / sweep_ms, 1)}
         log(f"sweep: {sweep_ms:.3f} ms -> {extra['sweep_64_layers']['GB/s']:.0f} GB/s")
-        del mats, xs, ys
+
+        # fused: per layer one launch for q+k+v (shared x), o, gate+up (shared x), down
+        nsh = len(synth.SWEEP_SHAPES)
+        groups = [[0, 1, 2], [3], [4, 5], [6]]
+        fcalls, ftotal = [], 0
+        for layer in range(synth.SWEEP_LAYERS):
+            for gidx in groups:
+                ws_ = [mats[layer * nsh + j][0] for j in gidx]
+                ns_ = [mats[layer * nsh + j][1] for j in gidx]
+                kk = mats[layer * nsh + gidx[0]][2]
+                xx = xs[layer * nsh + gidx[0]]
+                yy = [ys[layer * nsh + j] for j in gidx]
+                fcalls.append((ws_, ns_, kk, xx, yy))
+                ftotal += sum(n * synth.row_bytes(0, kk) for n in ns_) + kk * 2 + sum(ns_) * 4
+
+        def fsweep():
+            for ws_, ns_, kk, xx, yy in fcalls:
+                R.rfp4_gemv_multi(ws_, 0, ns_, kk, xx, yy)
+
+        fsweep()
+        g2 = torch.cuda.CUDAGraph()
+        s3 = torch.cuda.Stream()
+        s3.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s3):
+            fsweep()
+        torch.cuda.current_stream().wait_stream(s3)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g2):
+            fsweep()
+        g2.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g2.replay()
+        torch.cuda.synchronize()
+        fsweep_ms = (time.perf_counter() - t0) * 1e3 / reps
+        extra["sweep_64_layers_fused"] = {"GB/s": round(ftotal / (fsweep_ms * 1e-3) / 1e9, 1), "bytes": ftotal,
+                                          "ms_per_sweep": round(fsweep_ms, 3), "launches": len(fcalls),
+                                          "tokens_per_s_equivalent": round(1e3 / fsweep_ms, 1)}
+        log(f"sweep fused: {fsweep_ms:.3f} ms -> {extra['sweep_64_layers_fused']['GB/s']:.0f} GB/s")
+        del mats, xs, ys, fcalls, g, g2
         torch.cuda.empty_cache()
 
     # ---------------- CPU baseline: the fp64 oracle on the host

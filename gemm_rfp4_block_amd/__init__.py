@@ -26,7 +26,8 @@ RFP4_ERR_NONFINITE_SCALE = 4
 RFP4_ERR_HIP = 5
 
 EXPORTED = ("rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
-            "rfp4_dequant", "rfp4_gemv", "rfp4_gemm")
+            "rfp4_dequant", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm")
+MAX_GEMV_PARTS = 8
 
 
 class Rfp4Error(RuntimeError):
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.rfp4_dequant.restype = c_int
     L.rfp4_gemv.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_vp]
     L.rfp4_gemv.restype = c_int
+    L.rfp4_gemv_multi.argtypes = [c_int, ctypes.POINTER(c_vp), ctypes.POINTER(c_i64), c_int, c_i64, c_vp,
+                                  c_int, c_i64, c_i64, ctypes.POINTER(c_vp), ctypes.POINTER(c_i64), c_vp]
+    L.rfp4_gemv_multi.restype = c_int
     L.rfp4_gemm.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]
     L.rfp4_gemm.restype = c_int
     _lib = L
@@ -153,6 +157,27 @@ def rfp4_gemv(w, layout: int, n: int, k: int, x, y=None, stream=None):
     return y
 
 
+def rfp4_gemv_multi(ws, layout: int, ns, k: int, x, ys=None, stream=None):
+    """One launch of len(ws) matvecs sharing x: ys[i][b, r] = sum_c Ws[i][r, c] x[b, c]."""
+    import torch
+
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    batch = x.shape[0]
+    count = len(ws)
+    if ys is None:
+        ys = [torch.empty((batch, int(n)), dtype=torch.float32, device=x.device) for n in ns]
+    ldx = x.stride(0) if batch > 1 else max(k, x.stride(0))
+    ldy = [y.stride(0) if batch > 1 else max(int(n), y.stride(0)) for y, n in zip(ys, ns)]
+    wa = (ctypes.c_void_p * count)(*[w.data_ptr() for w in ws])
+    na = (ctypes.c_int64 * count)(*[int(n) for n in ns])
+    ya = (ctypes.c_void_p * count)(*[y.data_ptr() for y in ys])
+    la = (ctypes.c_int64 * count)(*ldy)
+    _check(lib().rfp4_gemv_multi(count, wa, na, layout, k, _ptr(x), _xdtype(x), batch, ldx, ya, la,
+                                 _stream(stream)), "rfp4_gemv_multi")
+    return ys
+
+
 def rfp4_gemm(w, layout: int, n: int, k: int, a, c=None, stream=None):
     """C = A W^T with A (m, k) bf16 and C (m, n) bf16 on the device."""
     import torch
@@ -168,5 +193,5 @@ def rfp4_gemm(w, layout: int, n: int, k: int, a, c=None, stream=None):
 __all__ = [
     "RFP4_DUAL", "RFP4_FAST", "RFP4_F16", "RFP4_BF16", "Rfp4Error", "lib", "library_path",
     "rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
-    "rfp4_dequant", "rfp4_gemv", "rfp4_gemm",
+    "rfp4_dequant", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm", "MAX_GEMV_PARTS",
 ]

@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = 2147483647;  // n, m, k <= 2^31 - 1
+static_assert(RFP4_MAX_GEMV_PARTS == rfp4::kMaxGemvParts, "parts limit of the header and the kernels");
 constexpr int64_t kMaxElems = int64_t(1) << 39;  // elements of A or C (2^40 bytes of bf16)
 
 bool layout_ok(int layout) { return layout == RFP4_DUAL || layout == RFP4_FAST; }
@@ -89,19 +90,36 @@ rfp4_status rfp4_dequant(const void* w, int layout, int64_t n, int64_t k, float*
                                        static_cast<hipStream_t>(stream)));
 }
 
+rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int64_t* n, int layout,
+                            int64_t k, const void* x, int xdtype, int64_t batch, int64_t ldx,
+                            float* const* y, const int64_t* ldy, void* stream) {
+  if (count < 1 || count > RFP4_MAX_GEMV_PARTS) return RFP4_ERR_SHAPE;
+  if (w == nullptr || n == nullptr || y == nullptr || ldy == nullptr) return RFP4_ERR_NULL;
+  rfp4::GemvPart parts[rfp4::kMaxGemvParts];
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) {
+    const rfp4_status st = check_weights(w[i], layout, n[i], k);
+    if (st != RFP4_OK) return st;
+    if (ldy[i] < n[i] || ldy[i] > kMaxDim) return RFP4_ERR_SHAPE;
+    if (y[i] == nullptr) return RFP4_ERR_NULL;
+    if (!aligned16(y[i])) return RFP4_ERR_UNSUPPORTED;
+    rows += n[i];
+    parts[i] = rfp4::GemvPart{static_cast<const uint8_t*>(w[i]), n[i], y[i], ldy[i]};
+  }
+  if (rows > kMaxDim) return RFP4_ERR_SHAPE;
+  if (xdtype != RFP4_F16 && xdtype != RFP4_BF16) return RFP4_ERR_UNSUPPORTED;
+  if (batch < 1 || batch > 8) return RFP4_ERR_SHAPE;
+  if (ldx < k || ldx > kMaxDim) return RFP4_ERR_SHAPE;
+  if (x == nullptr) return RFP4_ERR_NULL;
+  if (!aligned16(x) || (ldx % 8) != 0) return RFP4_ERR_UNSUPPORTED;
+  return from_hip(rfp4::launch_gemv(parts, count, layout, k, x, xdtype, static_cast<int>(batch),
+                                    ldx, static_cast<hipStream_t>(stream)));
+}
+
 rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const void* x,
                       int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,
                       void* stream) {
-  rfp4_status st = check_weights(w, layout, n, k);
-  if (st != RFP4_OK) return st;
-  if (xdtype != RFP4_F16 && xdtype != RFP4_BF16) return RFP4_ERR_UNSUPPORTED;
-  if (batch < 1 || batch > 8) return RFP4_ERR_SHAPE;
-  if (ldx < k || ldy < n || ldx > kMaxDim || ldy > kMaxDim) return RFP4_ERR_SHAPE;
-  if (x == nullptr || y == nullptr) return RFP4_ERR_NULL;
-  if (!aligned16(x) || !aligned16(y) || (ldx % 8) != 0) return RFP4_ERR_UNSUPPORTED;
-  return from_hip(rfp4::launch_gemv(static_cast<const uint8_t*>(w), layout, n, k, x, xdtype,
-                                    static_cast<int>(batch), ldx, y, ldy,
-                                    static_cast<hipStream_t>(stream)));
+  return rfp4_gemv_multi(1, &w, &n, layout, k, x, xdtype, batch, ldx, &y, &ldy, stream);
 }
 
 rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,

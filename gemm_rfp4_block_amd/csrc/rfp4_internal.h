@@ -25,9 +25,23 @@ int device_cu_count();
 hipError_t launch_dequant(const uint8_t* w, int layout, int64_t n, int64_t k, float* out,
                           int64_t ldo, hipStream_t stream);
 
-hipError_t launch_gemv(const uint8_t* w, int layout, int64_t n, int64_t k, const void* x,
-                       int xdtype, int batch, int64_t ldx, float* y, int64_t ldy,
-                       hipStream_t stream);
+// One matrix of a GEMV launch: n rows of packed weights at w, outputs y[b * ldy + r].
+constexpr int kMaxGemvParts = 8;
+struct GemvPart {
+  const uint8_t* w;
+  int64_t n;
+  float* y;
+  int64_t ldy;
+};
+
+// 1 <= count <= kMaxGemvParts matrices sharing k and the activations.
+hipError_t launch_gemv(const GemvPart* parts, int count, int layout, int64_t k, const void* x,
+                       int xdtype, int batch, int64_t ldx, hipStream_t stream);
+// The same for one activation dtype (nb = k / 32 blocks per row).
+hipError_t launch_gemv_f16(const GemvPart* parts, int count, int layout, int nb, const uint16_t* x,
+                           int batch, int64_t ldx, hipStream_t stream);
+hipError_t launch_gemv_bf16(const GemvPart* parts, int count, int layout, int nb, const uint16_t* x,
+                            int batch, int64_t ldx, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
                        int64_t m, int64_t lda, uint16_t* c, int64_t ldc, hipStream_t stream);

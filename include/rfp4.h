@@ -111,6 +111,23 @@ RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, 
                       int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,
                       void* stream);
 
+/* Several decode matvecs that share one activation batch, in one launch: the page's
+ * gemv_gate_up ("Kernel System"), also used for q/k/v. For i < count, part i computes
+ *   y[i][b * ldy[i] + r] = sum_c weight_i(r, c) * x[b * ldx + c],  r < n[i], b < batch
+ * as rfp4_gemv does for w[i], with the same layout and k for every part and the same
+ * accuracy (the lane mapping, and so the fp32 summation order, is chosen for the launch
+ * as a whole; with the same mapping the results equal separate rfp4_gemv calls bit for
+ * bit). The row groups of all parts are split evenly over the CUs, so small matrices
+ * (k/v) ride along with large ones. `w`, `n`, `y` and `ldy` are host arrays of
+ * `count` entries (1 <= count <= RFP4_MAX_GEMV_PARTS) holding device pointers and
+ * sizes; the total row count must be <= 2^31 - 1. Every part is checked as in
+ * rfp4_gemv before any HIP call. */
+#define RFP4_MAX_GEMV_PARTS 8
+RFP4_API rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int64_t* n,
+                                     int layout, int64_t k, const void* x, int xdtype,
+                                     int64_t batch, int64_t ldx, float* const* y,
+                                     const int64_t* ldy, void* stream);
+
 /* Weight-only 4-bit GEMM for prefill ("Kernel System": w4a16_gemm):
  *   c[i * ldc + r] = bf16_rne( sum_q a[i * lda + q] * weight(r, q) ),  i < m, r < n
  * i.e. C = A * W^T with A (m x k, bf16, row-major) and C (m x n, bf16, row-major);

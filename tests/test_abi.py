@@ -109,6 +109,41 @@ def test_gemv_argument_errors(L):
     assert f(P, 1, 8, 768, P2, 0, 1, 768, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # fast k % 512
 
 
+def test_gemv_multi_argument_errors(L):
+    import ctypes
+
+    f = L.rfp4_gemv_multi
+
+    def arr(t, vals):
+        return (t * len(vals))(*vals)
+
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    w2 = arr(vp, [P, P])
+    n2 = arr(i64, [8, 16])
+    y2 = arr(vp, [P, P])
+    l2 = arr(i64, [8, 16])
+    assert f(0, w2, n2, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_SHAPE  # count 0
+    assert f(R.MAX_GEMV_PARTS + 1, w2, n2, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_SHAPE
+    assert f(2, None, n2, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_NULL
+    assert f(2, w2, None, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_NULL
+    assert f(2, w2, n2, 0, 512, P2, 0, 1, 512, None, l2, NULL) == R.RFP4_ERR_NULL
+    assert f(2, w2, n2, 0, 512, P2, 0, 1, 512, y2, None, NULL) == R.RFP4_ERR_NULL
+    # one bad part is reported with that part's error
+    assert f(2, arr(vp, [P, NULL]), n2, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_NULL
+    assert f(2, w2, arr(i64, [8, 0]), 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_SHAPE
+    assert f(2, w2, n2, 0, 512, P2, 0, 1, 512, arr(vp, [P, UNALIGNED]), l2, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(2, w2, n2, 0, 512, P2, 0, 1, 512, y2, arr(i64, [8, 15]), NULL) == R.RFP4_ERR_SHAPE
+    assert f(2, arr(vp, [P, UNALIGNED]), n2, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED
+    # the total row count must fit in 2^31 - 1
+    big = 2**31 - 16
+    assert f(2, w2, arr(i64, [big, 32]), 0, 512, P2, 0, 1, 512, y2, arr(i64, [big, 32]), NULL) == R.RFP4_ERR_SHAPE
+    # shared arguments are checked as in rfp4_gemv
+    assert f(2, w2, n2, 0, 512, P2, 2, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED  # dtype
+    assert f(2, w2, n2, 0, 512, P2, 0, 9, 512, y2, l2, NULL) == R.RFP4_ERR_SHAPE  # batch
+    assert f(2, w2, n2, 0, 512, NULL, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_NULL  # x
+    assert f(2, w2, n2, 0, 512, UNALIGNED, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED
+
+
 def test_gemm_argument_errors(L):
     f = L.rfp4_gemm
     assert f(NULL, 0, 64, 512, P2, 16, 512, P, 64, NULL) == R.RFP4_ERR_NULL
