@@ -198,6 +198,15 @@ def main():
     # dispatch gap, so these are upper bounds).
     durs = timed_launches(torch, lambda i: R.rfp4_gemv(copies[i % nc], layout, n, k, x, y), args.steps)
     st = stats_us(durs)
+    # back-to-back launches without a graph, one event pair around all of them
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        R.rfp4_gemv(copies[i % nc], layout, n, k, x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    direct_us = e0.elapsed_time(e1) * 1e3 / args.steps
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -213,7 +222,9 @@ def main():
         f"events over timed region {launch_us:.2f} us/launch -> {achieved:.0f} GB/s "
         f"({achieved / HBM_PEAK_GBS:.1%}); single-launch events mean {st['mean_us']:.2f} us")
 
-    extra = {"gemv_up_graph_replay_matches_eager": replay_ok}
+    extra = {"gemv_up_graph_replay_matches_eager": replay_ok,
+             "gemv_up_direct_launches": {"us_per_launch": round(direct_us, 3),
+                                         "GB/s": round(alg_bytes / (direct_us * 1e-6) / 1e9, 1)}}
     del copies
     torch.cuda.empty_cache()
 
@@ -246,7 +257,15 @@ def main():
     extra["dequant_up"] = {"GB/s": round(dq_bytes / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": dq_bytes,
                            "mean_us": round(d["mean_us"], 2)}
     log(f"dequant: {d['mean_us']:.1f} us -> {extra['dequant_up']['GB/s']:.0f} GB/s")
-    del out
+    outb = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        R.rfp4_dequant_bf16(wq, layout, n, k, outb)
+    d = stats_us(timed_launches(torch, lambda i: R.rfp4_dequant_bf16(wq, layout, n, k, outb), 20))
+    dqb_bytes = w_bytes + n * k * 2
+    extra["dequant_bf16_up"] = {"GB/s": round(dqb_bytes / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": dqb_bytes,
+                                "mean_us": round(d["mean_us"], 2)}
+    log(f"dequant bf16: {d['mean_us']:.1f} us -> {extra['dequant_bf16_up']['GB/s']:.0f} GB/s")
+    del out, outb
     torch.cuda.empty_cache()
 
     # ---------------- prefill GEMM
@@ -266,7 +285,17 @@ def main():
                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
                 **{kk: round(v, 2) for kk, v in d.items()}}
         log(f"gemm: mean {d['mean_us']:.1f} us -> {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
-        del wg, a, c
+        # the dequantize-then-multiply baseline (bf16 expansion + rocBLAS dense GEMM)
+        wbuf = torch.empty((gn, gk), dtype=torch.bfloat16, device=dev)
+        call_fb = lambda i: R.rfp4_gemm_dequant(wg, gcfg["layout"], gn, gk, a, wbuf, c)
+        warm_up(torch, call_fb)
+        dfb = stats_us(timed_launches(torch, call_fb, 30))
+        gemm["dequant_then_dense_baseline"] = {
+            "TFLOP/s": round(flops / (dfb["mean_us"] * 1e-6) / 1e12, 1), "mean_us": round(dfb["mean_us"], 2),
+            "what": "rfp4_gemm_dequant: bf16 expansion of W (178 MB written) + rocBLAS dense bf16 GEMM"}
+        log(f"gemm dequant+dense baseline: mean {dfb['mean_us']:.1f} us -> "
+            f"{gemm['dequant_then_dense_baseline']['TFLOP/s']:.1f} TFLOP/s")
+        del wg, a, c, wbuf
         torch.cuda.empty_cache()
 
     # ---------------- fused multi-matrix GEMVs (gate + up, q + k + v), one launch each

@@ -26,7 +26,8 @@ RFP4_ERR_NONFINITE_SCALE = 4
 RFP4_ERR_HIP = 5
 
 EXPORTED = ("rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
-            "rfp4_dequant", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm")
+            "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
+            "rfp4_gemm_dequant")
 MAX_GEMV_PARTS = 8
 
 
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.rfp4_gemv_multi.restype = c_int
     L.rfp4_gemm.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]
     L.rfp4_gemm.restype = c_int
+    L.rfp4_dequant_bf16.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_vp]
+    L.rfp4_dequant_bf16.restype = c_int
+    L.rfp4_gemm_dequant.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]
+    L.rfp4_gemm_dequant.restype = c_int
     _lib = L
     return L
 
@@ -141,6 +146,17 @@ def rfp4_dequant(w, layout: int, n: int, k: int, out=None, ldo: int | None = Non
     return out
 
 
+def rfp4_dequant_bf16(w, layout: int, n: int, k: int, out=None, stream=None):
+    """W as an (n, k) bf16 device tensor (bit-exact)."""
+    import torch
+
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
+    _check(lib().rfp4_dequant_bf16(_ptr(w), layout, n, k, _ptr(out), out.stride(0), _stream(stream)),
+           "rfp4_dequant_bf16")
+    return out
+
+
 def rfp4_gemv(w, layout: int, n: int, k: int, x, y=None, stream=None):
     """y[b, r] = sum_c W[r, c] x[b, c]; ``x`` (batch, k) f16/bf16 on the device, y fp32."""
     import torch
@@ -190,8 +206,24 @@ def rfp4_gemm(w, layout: int, n: int, k: int, a, c=None, stream=None):
     return c
 
 
+def rfp4_gemm_dequant(w, layout: int, n: int, k: int, a, wbuf=None, c=None, stream=None):
+    """C = A W^T computed as bf16 dequantization into ``wbuf`` (n, k) plus a dense bf16
+    GEMM (rocBLAS)."""
+    import torch
+
+    m = a.shape[0]
+    if c is None:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    if wbuf is None:
+        wbuf = torch.empty((n, k), dtype=torch.bfloat16, device=a.device)
+    _check(lib().rfp4_gemm_dequant(_ptr(w), layout, n, k, _ptr(a), m, a.stride(0), _ptr(c), c.stride(0),
+                                   _ptr(wbuf), wbuf.stride(0), _stream(stream)), "rfp4_gemm_dequant")
+    return c
+
+
 __all__ = [
     "RFP4_DUAL", "RFP4_FAST", "RFP4_F16", "RFP4_BF16", "Rfp4Error", "lib", "library_path",
     "rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
-    "rfp4_dequant", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm", "MAX_GEMV_PARTS",
+    "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
+    "rfp4_gemm_dequant", "MAX_GEMV_PARTS",
 ]

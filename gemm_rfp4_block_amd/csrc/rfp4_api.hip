@@ -122,8 +122,21 @@ rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const voi
   return rfp4_gemv_multi(1, &w, &n, layout, k, x, xdtype, batch, ldx, &y, &ldy, stream);
 }
 
-rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
-                      int64_t m, int64_t lda, void* c, int64_t ldc, void* stream) {
+rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int64_t k, uint16_t* out,
+                              int64_t ldo, void* stream) {
+  rfp4_status st = check_weights(w, layout, n, k);
+  if (st != RFP4_OK) return st;
+  if (ldo < k || ldo > kMaxElems / n) return RFP4_ERR_SHAPE;
+  if (out == nullptr) return RFP4_ERR_NULL;
+  if (!aligned16(out) || (ldo % 8) != 0) return RFP4_ERR_UNSUPPORTED;
+  return from_hip(rfp4::launch_dequant_bf16(static_cast<const uint8_t*>(w), layout, n, k, out, ldo,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+// Shared checks of the GEMM entry points (weights, A, C).
+rfp4_status check_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a, int64_t m,
+                       int64_t lda, const void* c, int64_t ldc) {
   rfp4_status st = check_weights(w, layout, n, k);
   if (st != RFP4_OK) return st;
   if (m < 1 || m > kMaxDim) return RFP4_ERR_SHAPE;
@@ -132,6 +145,29 @@ rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const voi
   if (a == nullptr || c == nullptr) return RFP4_ERR_NULL;
   if (!aligned16(a) || !aligned16(c) || (lda % 8) != 0 || (ldc % 8) != 0)
     return RFP4_ERR_UNSUPPORTED;
+  return RFP4_OK;
+}
+}  // namespace
+
+rfp4_status rfp4_gemm_dequant(const void* w, int layout, int64_t n, int64_t k, const void* a,
+                              int64_t m, int64_t lda, void* c, int64_t ldc, uint16_t* wbuf,
+                              int64_t ldw, void* stream) {
+  rfp4_status st = check_gemm(w, layout, n, k, a, m, lda, c, ldc);
+  if (st != RFP4_OK) return st;
+  if (ldw < k || ldw > kMaxElems / n) return RFP4_ERR_SHAPE;
+  if (wbuf == nullptr) return RFP4_ERR_NULL;
+  if (!aligned16(wbuf) || (ldw % 8) != 0) return RFP4_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = from_hip(rfp4::launch_dequant_bf16(static_cast<const uint8_t*>(w), layout, n, k, wbuf, ldw, s));
+  if (st != RFP4_OK) return st;
+  return static_cast<rfp4_status>(rfp4::dense_gemm_bf16(wbuf, n, k, ldw, static_cast<const uint16_t*>(a),
+                                                        m, lda, static_cast<uint16_t*>(c), ldc, s));
+}
+
+rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
+                      int64_t m, int64_t lda, void* c, int64_t ldc, void* stream) {
+  rfp4_status st = check_gemm(w, layout, n, k, a, m, lda, c, ldc);
+  if (st != RFP4_OK) return st;
   return from_hip(rfp4::launch_gemm(static_cast<const uint8_t*>(w), layout, n, k,
                                     static_cast<const uint16_t*>(a), m, lda,
                                     static_cast<uint16_t*>(c), ldc,

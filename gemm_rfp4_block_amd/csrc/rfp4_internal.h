@@ -24,6 +24,13 @@ int device_cu_count();
 // 16-byte aligned, pointers non-null and aligned as the public header requires.
 hipError_t launch_dequant(const uint8_t* w, int layout, int64_t n, int64_t k, float* out,
                           int64_t ldo, hipStream_t stream);
+hipError_t launch_dequant_bf16(const uint8_t* w, int layout, int64_t n, int64_t k, uint16_t* out,
+                               int64_t ldo, hipStream_t stream);
+
+// Dense bf16 C = A W^T through rocBLAS (loaded at first use); RFP4 status codes:
+// 0 = ok, RFP4_ERR_UNSUPPORTED when rocBLAS is unavailable, RFP4_ERR_HIP on failure.
+int dense_gemm_bf16(const uint16_t* wb, int64_t n, int64_t k, int64_t ldw, const uint16_t* a,
+                    int64_t m, int64_t lda, uint16_t* c, int64_t ldc, hipStream_t stream);
 
 // One matrix of a GEMV launch: n rows of packed weights at w, outputs y[b * ldy + r].
 constexpr int kMaxGemvParts = 8;

@@ -23,11 +23,11 @@
  *
  * General rules for every entry point:
  *   - All pointers except rfp4_validate's `w_host` are device pointers. The caller
- *     owns every buffer it passes. rfp4_dequant and rfp4_gemv never allocate, free
- *     or synchronize; rfp4_gemm may use a workspace of its own (see there). Global
- *     state: per-device caches of the CU count and of kernel attributes (atomics)
- *     and rfp4_gemm's workspaces (behind a mutex), so calls from several threads
- *     are safe.
+ *     owns every buffer it passes. The dequant and GEMV entry points never
+ *     allocate, free or synchronize; rfp4_gemm may use a workspace of its own and
+ *     rfp4_gemm_dequant uses rocBLAS (see there). Global state: per-device caches of
+ *     the CU count and of kernel attributes (atomics), rfp4_gemm's workspaces and
+ *     the rocBLAS handles (behind mutexes), so calls from several threads are safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are
  *     asynchronous and ordered on that stream; a fault in a kernel surfaces at the
  *     caller's next synchronization.
@@ -102,6 +102,13 @@ RFP4_API rfp4_status rfp4_validate(const uint8_t* w_host, int layout, int64_t n,
 RFP4_API rfp4_status rfp4_dequant(const void* w, int layout, int64_t n, int64_t k, float* out,
                          int64_t ldo, void* stream);
 
+/* Dequantization to bf16: out[r * ldo + c] = weight (r, c) as bf16 bits, bit-exact
+ * (every codebook value times every decoded scale is a bf16 value; signs of zero as
+ * rfp4_dequant). `out` has n rows of ldo bf16 values, ldo >= k, ldo % 8 == 0,
+ * 16-byte aligned, n * ldo <= 2^39. */
+RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int64_t k,
+                                       uint16_t* out, int64_t ldo, void* stream);
+
 /* Decode matvec, the page's decode hot path ("Kernel System": gemv; "Integration
  * Options", Option 2): for b < batch and r < n,
  *   y[b * ldy + r] = sum_c weight(r, c) * x[b * ldx + c]
@@ -147,6 +154,18 @@ RFP4_API rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int6
  * (128 x 128 tiles only, k unsplit or split 2 or 4 ways), "nosplit". */
 RFP4_API rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
                       int64_t m, int64_t lda, void* c, int64_t ldc, void* stream);
+
+/* Dequantize-then-multiply prefill, the comparison baseline of rfp4_gemm ("Kernel
+ * System" lists dequantize + dense GEMM beside the fused w4a16_gemm): W is expanded
+ * to bf16 into the caller's buffer `wbuf` (n rows of ldw bf16 values, ldw >= k,
+ * ldw % 8 == 0, 16-byte aligned; it holds rfp4_dequant_bf16's result afterwards) and
+ * C = A W^T is computed by rocBLAS's dense bf16 GEMM (fp32 accumulation, bf16
+ * output), on `stream`. Same arguments and checks as rfp4_gemm otherwise. rocBLAS is
+ * loaded at the first call (RFP4_ERR_UNSUPPORTED if it cannot be); one rocBLAS handle
+ * is kept per (device, stream), and rocBLAS may hold workspace memory of its own. */
+RFP4_API rfp4_status rfp4_gemm_dequant(const void* w, int layout, int64_t n, int64_t k,
+                                       const void* a, int64_t m, int64_t lda, void* c,
+                                       int64_t ldc, uint16_t* wbuf, int64_t ldw, void* stream);
 
 #ifdef __cplusplus
 }

@@ -144,6 +144,32 @@ def test_gemv_multi_argument_errors(L):
     assert f(2, w2, n2, 0, 512, UNALIGNED, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED
 
 
+def test_dequant_bf16_argument_errors(L):
+    f = L.rfp4_dequant_bf16
+    assert f(NULL, 0, 8, 512, P, 512, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 8, 512, NULL, 512, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 8, 512, P, 511, NULL) == R.RFP4_ERR_SHAPE  # ldo < k
+    assert f(P, 0, 8, 512, P, 516, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldo % 8
+    assert f(P, 0, 8, 512, UNALIGNED, 512, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 5, 8, 512, P, 512, NULL) == R.RFP4_ERR_UNSUPPORTED  # layout
+    assert f(P, 0, 8, 500, P, 512, NULL) == R.RFP4_ERR_SHAPE  # k % 32
+    assert f(P, 0, 2**20, 512, P, 2**20, NULL) == R.RFP4_ERR_SHAPE  # n * ldo > 2^39
+
+
+def test_gemm_dequant_argument_errors(L):
+    f = L.rfp4_gemm_dequant
+    ok = (P, 0, 64, 512, P2, 16, 512, P, 64)
+    assert f(*ok, NULL, 512, NULL) == R.RFP4_ERR_NULL  # wbuf
+    assert f(*ok, P2, 511, NULL) == R.RFP4_ERR_SHAPE  # ldw < k
+    assert f(*ok, P2, 520 + 4, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldw % 8
+    assert f(*ok, UNALIGNED, 512, NULL) == R.RFP4_ERR_UNSUPPORTED
+    # the GEMM arguments are checked as in rfp4_gemm, before wbuf
+    assert f(NULL, 0, 64, 512, P2, 16, 512, P, 64, NULL, 512, NULL) == R.RFP4_ERR_NULL
+    assert f(P, 0, 64, 512, P2, 0, 512, P, 64, P2, 512, NULL) == R.RFP4_ERR_SHAPE  # m = 0
+    assert f(P, 0, 64, 512, P2, 16, 512, P, 63, P2, 512, NULL) == R.RFP4_ERR_SHAPE  # ldc < n
+    assert f(P, 0, 64, 512, P2, 16, 516, P, 64, P2, 512, NULL) == R.RFP4_ERR_UNSUPPORTED  # lda % 8
+
+
 def test_gemm_argument_errors(L):
     f = L.rfp4_gemm
     assert f(NULL, 0, 64, 512, P2, 16, 512, P, 64, NULL) == R.RFP4_ERR_NULL

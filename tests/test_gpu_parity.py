@@ -107,6 +107,60 @@ def test_dequant_padded_ldo():
     assert np.all(o[:, k:] == -7.0)
 
 
+def bf16_bits_of(f32):
+    """bf16 encodings of fp32 values that are bf16 values (asserted: low 16 bits zero)."""
+    u = bits(f32)
+    assert np.all((u & 0xFFFF) == 0), "value not representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def dequant_bf16_bits(w, layout, n, k, out=None):
+    o = R.rfp4_dequant_bf16(dev(w), layout, n, k, out=out)
+    torch.cuda.synchronize()
+    return o.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_dequant_bf16_every_scale_byte_and_index(layout):
+    """As the fp32 test: every scale byte, every index in both nibble positions, bf16
+    output compared bit for bit (signs of zero included)."""
+    k = 512
+    nb = k // 32
+    qs = np.array([t | ((15 - t) << 4) for t in range(16)], dtype=np.uint8)
+    rows = []
+    for b in range(256):
+        blk = []
+        for j in range(nb):
+            q = np.roll(qs, 3 * j)
+            sc = [b, (b * 37 + 11) % 256] if layout == 0 else [b]
+            blk.append(np.concatenate([q, sc]).astype(np.uint8))
+        rows.append(np.concatenate(blk))
+    w = np.stack(rows)
+    got = dequant_bf16_bits(w, layout, 256, k)
+    assert np.array_equal(got, bf16_bits_of(O.dequantize_f32(w, layout, 256, k)))
+
+
+@pytest.mark.parametrize("name", ["up", "down"])
+def test_dequant_bf16_full_size_bitwise(name):
+    w, _, cfg = synth.gemv_inputs(name)
+    n, k = cfg["n"], cfg["k"]
+    got = dequant_bf16_bits(w, cfg["layout"], n, k)
+    assert np.array_equal(got, bf16_bits_of(O.dequantize_f32(w, cfg["layout"], n, k)))
+
+
+def test_dequant_bf16_padded_ldo():
+    rng = np.random.default_rng(22)
+    n, k, ldo = 21, 1024, 1048
+    w = synth.weights(rng, 0, n, k, stress_frac=0.05)
+    out = torch.full((n, ldo), -3.0, dtype=torch.bfloat16, device=DEV)
+    got = R.rfp4_dequant_bf16(dev(w), 0, n, k, out=out[:, :k])
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(o[:, :k], bf16_bits_of(O.dequantize_f32(w, 0, n, k)))
+    assert np.all(out[:, k:].float().cpu().numpy() == -3.0)
+    assert got.data_ptr() == out.data_ptr()
+
+
 # ------------------------------------------------------------------ GEMV
 
 def check_gemv(w, layout, n, k, x, **kw):
@@ -388,6 +442,34 @@ def test_gemm_mixed_tile_sizes():
     c = run_gemm(w, layout, n, k, a)
     c_ref, den = O.gemm(w, layout, n, k, x64(a))
     assert gemm_error(c, c_ref, den) <= TOL
+
+
+@pytest.mark.parametrize("case", [(0, 100, 200, 512), (1, 77, 136, 1024), (0, 257, 520, 2304)],
+                         ids=lambda c: "L{}m{}n{}k{}".format(*c))
+def test_gemm_dequant_fallback(case):
+    """Dequantize to bf16 + dense GEMM: same tolerance as the fused GEMM; the bf16
+    weight buffer holds the exact dequantization afterwards."""
+    layout, m, n, k = case
+    rng = np.random.default_rng(7000 + m + n + k)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    a = synth.activations(rng, m, k, "bf16")
+    wbuf = torch.empty((n, k), dtype=torch.bfloat16, device=DEV)
+    c = R.rfp4_gemm_dequant(dev(w), layout, n, k, a.to(DEV).contiguous(), wbuf=wbuf)
+    torch.cuda.synchronize()
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c.to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
+    wb = wbuf.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(wb, bf16_bits_of(O.dequantize_f32(w, layout, n, k)))
+
+
+def test_gemm_dequant_full_size_sampled():
+    w, a, cfg = synth.gemm_inputs("prefill")
+    n, k, m = cfg["n"], cfg["k"], cfg["m"]
+    c = R.rfp4_gemm_dequant(dev(w), cfg["layout"], n, k, a.to(DEV).contiguous())
+    torch.cuda.synchronize()
+    cols = np.sort(np.random.default_rng(98).choice(n, size=64, replace=False))
+    c_ref, den = O.gemm_rows(w, cfg["layout"], n, k, x64(a), cols)
+    assert gemm_error(c[:, cols].to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
 
 
 def test_gemm_full_size_sampled():
