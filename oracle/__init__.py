@@ -20,6 +20,7 @@ from .rfp4_oracle import (  # noqa: F401
     gemv_rows,
     nibble_indices,
     normalized_error,
+    quantize,
     row_bytes,
     scale_value,
     split_blocks,

@@ -39,6 +39,10 @@ taken here (each also listed with its reason in the design notes):
           of a row covers columns 32j .. 32j+31; rows are packed back to back.
   R-OUT   GEMV output fp32, GEMM output bf16 (rounded to nearest even); both
           accumulate in fp32 on the device. The oracle computes the exact result in fp64.
+  R-QUANT the encoder (``quantize``): smallest finite half-scale reaching the group's
+          largest magnitude with code 10, then the nearest codebook entry, ties to the
+          smaller magnitude. The page gives no encoder; pinned by the decode round trip
+          and by brute-force nearest-entry and minimal-scale checks.
 
 Pins (tests under tests/ marked "not gpu"): the printed block sizes and bits per
 weight, the printed codebook, E4M3 on all 256 bytes against the textbook closed form
@@ -194,6 +198,48 @@ def gemm_rows(w: np.ndarray, layout: int, n: int, k: int, a: np.ndarray, cols: n
     rb = row_bytes(layout, k)
     wr = np.ascontiguousarray(np.asarray(w, dtype=np.uint8).reshape(n, rb)[cols])
     return gemm(wr, layout, len(cols), k, a)
+
+
+# ------------------------------------------------------------------ quantizer
+# The page defines the value a block decodes to but no encoder; of encoding it says only
+# that the largest magnitude was retuned from 12 to 10 to limit the pull of outliers
+# ("Codebook10 Value Table"). Reading R-QUANT, the plainest encoder the decoder supports:
+#   * a group (a 16-weight half for dual, the whole block for fast) takes the smallest
+#     finite half-scale S(b), b in 0..126 (bit 7 clear; 0x7F is non-finite), with
+#     10 * S(b) >= max |w| over the group, saturating at b = 126 (S = 224);
+#   * each weight takes the codebook entry nearest to w / S: its magnitude index is the
+#     number of midpoints m of consecutive magnitudes with |w| > m * S (a tie goes to the
+#     smaller magnitude), and its sign bit is set when w < 0 and the magnitude is not 0
+#     (a zero, of either sign, is index 0).
+# Every 10 * S(b) and m * S(b) is exact in fp32 and fp64, so no rounding decides a code
+# and any implementation that compares exactly gets the same bytes.
+MAX_FINITE_SCALE_BYTE = 126
+MIDPOINTS = (0.5, 1.5, 2.5, 3.5, 5.0, 7.0, 9.0)  # between 0,1,2,3,4,6,8,10
+
+
+def quantize(v, layout: int) -> np.ndarray:
+    """Encode real weights (n, k), k % 32 == 0, to packed blocks (n, row_bytes) (R-QUANT).
+
+    Inputs are used exactly (fp16/bf16/fp32 all convert exactly to fp64); non-finite
+    inputs give unspecified bytes."""
+    v = np.asarray(v, dtype=np.float64)
+    n, k = v.shape
+    if k % WEIGHTS_PER_BLOCK:
+        raise ValueError("k must be a multiple of 32")
+    nb = k // WEIGHTS_PER_BLOCK
+    group = 16 if layout == DUAL else 32
+    g = v.reshape(n, nb, WEIGHTS_PER_BLOCK // group, group)
+    amax = np.abs(g).max(axis=-1)
+    reach = 10.0 * scale_value(np.arange(MAX_FINITE_SCALE_BYTE + 1))  # strictly increasing
+    b = np.minimum(np.searchsorted(reach, amax, side="left"), MAX_FINITE_SCALE_BYTE)
+    s = scale_value(b)[..., None]
+    mag = np.zeros(g.shape, dtype=np.int64)
+    for m in MIDPOINTS:
+        mag += np.abs(g) > m * s
+    idx = (mag + 8 * ((g < 0) & (mag > 0))).reshape(n, nb, WEIGHTS_PER_BLOCK)
+    qs = (idx[..., :16] | (idx[..., 16:] << 4)).astype(np.uint8)  # R-NIB
+    e = b.astype(np.uint8).reshape(n, nb, scale_bytes_per_block(layout))
+    return np.concatenate([qs, e], axis=-1).reshape(n, nb * block_bytes(layout))
 
 
 def validate(w: np.ndarray, layout: int, n: int, k: int):

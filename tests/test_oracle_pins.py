@@ -235,9 +235,82 @@ def check_gemm_orientation(seed=5):
     assert c.shape == (m, n) and np.array_equal(c, y)
 
 
+def unpack_blocks(w: np.ndarray, layout: int, n: int, k: int):
+    """Test-owned unpacker (inverse of pack_blocks): (idx (n, nb, 32), sbytes (n, nb, ns))."""
+    nb = k // 32
+    bb = 18 if layout == O.DUAL else 17
+    blk = np.asarray(w, dtype=np.uint8).reshape(n, nb, bb).astype(np.int64)
+    idx = np.concatenate([blk[:, :, :16] & 15, blk[:, :, :16] >> 4], axis=2)
+    return idx, blk[:, :, 16:]
+
+
+def check_quantize_roundtrip(seed=6):
+    """Encoding the exact values of blocks whose every scale group holds a +-10 code (and no
+    index 8, the second zero) gives back the same bytes: the encoder inverts the
+    printed codebook, torch's E4M3 and the nibble convention."""
+    rng = np.random.default_rng(seed)
+    for layout in (O.DUAL, O.FAST):
+        n, k = 5, 256
+        nb, g = k // 32, (16 if layout == O.DUAL else 32)
+        ns = 32 // g
+        idx = rng.choice([i for i in range(16) if i != 8], size=(n, nb, 32))
+        for r in range(n):
+            for j in range(nb):
+                for h in range(ns):
+                    idx[r, j, h * g + rng.integers(0, g)] = rng.choice([7, 15])
+        sb = rng.integers(1, 127, size=(n, nb, ns))
+        w = pack_blocks(idx, sb, layout)
+        vals = np.array([[float(v) for v in row] for row in exact_weights(idx, sb, layout)])
+        assert np.array_equal(O.quantize(vals, layout), w)
+
+
+def check_quantize_nearest_minimal(seed=7):
+    """Brute force on random values, exact ties and extremes: each group's scale is the
+    smallest finite one that reaches its largest magnitude with code 10, and each weight's
+    code is the codebook entry nearest to it (ties to the smaller magnitude, zero as
+    index 0). Exact rational arithmetic throughout."""
+    rng = np.random.default_rng(seed)
+    for layout in (O.DUAL, O.FAST):
+        n, k = 4, 128
+        v = rng.standard_normal((n, k)) * np.exp2(rng.integers(-12, 12, size=(n, 1)))
+        v[0, :32] = 0.0
+        v[0, 5] = -0.0
+        v[1, :32] = np.float32(1e6) * np.sign(rng.standard_normal(32))
+        s3 = 0.5 * float(torch_e4m3_magnitude(0x3B))  # a normal scale
+        ties = np.array([0.5, 1.5, 2.5, 3.5, 5.0, 7.0, 9.0, 10.0, -0.5, -9.0, 4.0, -6.0, 1.0, 2.0, 3.0, 8.0])
+        v[2, :32] = np.concatenate([ties, -ties]) * s3
+        v[3, :32] = 1e-30 * np.arange(32)
+        q = O.quantize(v, layout)
+        idx, sb = unpack_blocks(q, layout, n, k)
+        g = 16 if layout == O.DUAL else 32
+        half = [Fraction(0)] + [torch_e4m3_magnitude(u) / 2 for u in range(1, 127)]
+        for r in range(n):
+            for j in range(k // 32):
+                for h in range(32 // g):
+                    b = int(sb[r, j, h])
+                    assert b <= 126
+                    grp = [Fraction(float(x)) for x in v[r, 32 * j + h * g: 32 * j + (h + 1) * g]]
+                    amax = max(abs(x) for x in grp)
+                    if amax <= 10 * half[126]:
+                        assert 10 * half[b] >= amax and (b == 0 or 10 * half[b - 1] < amax)
+                    else:
+                        assert b == 126
+                    S = half[b]
+                    for t, x in enumerate(grp):
+                        i = int(idx[r, j, h * g + t])
+                        best = min(range(16), key=lambda c: (abs(x - PRINTED_CB[c] * S), abs(PRINTED_CB[c]), c))
+                        assert abs(x - PRINTED_CB[i] * S) == abs(x - PRINTED_CB[best] * S)
+                        assert abs(PRINTED_CB[i]) == abs(PRINTED_CB[best])
+                        if PRINTED_CB[i] == 0:
+                            assert i == 0
+                        else:
+                            assert (i >= 8) == (x < 0)
+
+
 ALL_CHECKS = [check_block_layout, check_codebook, check_e4m3, check_scale, check_witness,
               check_fraction_dequant_and_gemv, check_fraction_gemm, check_special_cases,
-              check_invariants, check_gemm_orientation]
+              check_invariants, check_gemm_orientation, check_quantize_roundtrip,
+              check_quantize_nearest_minimal]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -351,7 +424,38 @@ def _mut_gemm_dropped_block(w, layout, n, k, a):
     return a @ wd.T, np.abs(a) @ np.abs(wd).T
 
 
+def _mut_quant_ties_up(v, layout):
+    """Ties go to the larger magnitude."""
+    eps = 1e-12
+    return _orig_quantize(np.asarray(v, dtype=np.float64) * (1 + eps), layout)
+
+
+def _mut_quant_scale_one_up(v, layout):
+    q = _orig_quantize(v, layout).copy()
+    n, k = np.asarray(v).shape
+    bb = 18 if layout == O.DUAL else 17
+    blk = q.reshape(n, k // 32, bb)
+    blk[:, :, 16:] = np.minimum(blk[:, :, 16:] + 1, 126)
+    return q
+
+
+def _mut_quant_planes_swapped(v, layout):
+    q = _orig_quantize(v, layout).copy()
+    n, k = np.asarray(v).shape
+    bb = 18 if layout == O.DUAL else 17
+    blk = q.reshape(n, k // 32, bb)
+    blk[:, :, :16] = (blk[:, :, :16] >> 4) | ((blk[:, :, :16] & 15) << 4)
+    return q
+
+
+_orig_quantize = O.quantize
+
 MUTATIONS = {
+    "quant_midpoint_5_to_5.5": ("MIDPOINTS", (0.5, 1.5, 2.5, 3.5, 5.5, 7.0, 9.0)),
+    "quant_allows_nonfinite_byte": ("MAX_FINITE_SCALE_BYTE", 127),
+    "quant_ties_to_larger": ("quantize", _mut_quant_ties_up),
+    "quant_scale_one_step_up": ("quantize", _mut_quant_scale_one_up),
+    "quant_nibble_planes_swapped": ("quantize", _mut_quant_planes_swapped),
     "sequential_nibbles": ("nibble_indices", _mut_sequential_nibbles),
     "swapped_nibble_planes": ("nibble_indices", _mut_swapped_planes),
     "codebook_12": ("CODEBOOK10", np.array([0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12])),
