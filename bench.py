@@ -265,7 +265,19 @@ def main():
     extra["dequant_bf16_up"] = {"GB/s": round(dqb_bytes / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": dqb_bytes,
                                 "mean_us": round(d["mean_us"], 2)}
     log(f"dequant bf16: {d['mean_us']:.1f} us -> {extra['dequant_bf16_up']['GB/s']:.0f} GB/s")
-    del out, outb
+    # encoder (rfp4_quantize) on the same shape, bf16 source: reads 2 bytes, writes
+    # 18/32 bytes per weight
+    src = synth.real_weights(np.random.default_rng(3), n, k, "bf16").to(dev)
+    wq2 = torch.empty_like(wq)
+    call_q = lambda i: R.rfp4_quantize(src, layout, wq2)
+    for _ in range(3):
+        call_q(0)
+    d = stats_us(timed_launches(torch, call_q, 20))
+    q_bytes = n * k * 2 + w_bytes
+    extra["quantize_bf16_up"] = {"GB/s": round(q_bytes / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": q_bytes,
+                                 "mean_us": round(d["mean_us"], 2)}
+    log(f"quantize bf16: {d['mean_us']:.1f} us -> {extra['quantize_bf16_up']['GB/s']:.0f} GB/s")
+    del out, outb, src, wq2
     torch.cuda.empty_cache()
 
     # ---------------- prefill GEMM

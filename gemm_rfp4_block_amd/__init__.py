@@ -17,6 +17,7 @@ RFP4_DUAL = 0
 RFP4_FAST = 1
 RFP4_F16 = 0
 RFP4_BF16 = 1
+RFP4_F32 = 2
 
 RFP4_OK = 0
 RFP4_ERR_NULL = 1
@@ -27,7 +28,7 @@ RFP4_ERR_HIP = 5
 
 EXPORTED = ("rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
             "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
-            "rfp4_gemm_dequant")
+            "rfp4_gemm_dequant", "rfp4_quantize")
 MAX_GEMV_PARTS = 8
 
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.rfp4_dequant_bf16.restype = c_int
     L.rfp4_gemm_dequant.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]
     L.rfp4_gemm_dequant.restype = c_int
+    L.rfp4_quantize.argtypes = [c_vp, c_int, c_i64, c_i64, c_i64, c_int, c_vp, c_vp]
+    L.rfp4_quantize.restype = c_int
     _lib = L
     return L
 
@@ -221,9 +224,27 @@ def rfp4_gemm_dequant(w, layout: int, n: int, k: int, a, wbuf=None, c=None, stre
     return c
 
 
+def rfp4_quantize(src, layout: int, out=None, stream=None):
+    """Encode ``src`` (n, k) float32/bfloat16/float16 on the device into packed rows
+    (uint8 tensor of shape (n, row_bytes))."""
+    import torch
+
+    codes = {torch.float32: RFP4_F32, torch.bfloat16: RFP4_BF16, torch.float16: RFP4_F16}
+    if src.dtype not in codes:
+        raise TypeError(f"src must be float32, bfloat16 or float16, got {src.dtype}")
+    n, k = src.shape
+    if src.stride(1) != 1:
+        raise ValueError("src rows must be contiguous")
+    if out is None:
+        out = torch.empty((n, max(rfp4_row_bytes(layout, k), 0)), dtype=torch.uint8, device=src.device)
+    _check(lib().rfp4_quantize(_ptr(src), codes[src.dtype], n, k, src.stride(0), layout, _ptr(out),
+                               _stream(stream)), "rfp4_quantize")
+    return out
+
+
 __all__ = [
     "RFP4_DUAL", "RFP4_FAST", "RFP4_F16", "RFP4_BF16", "Rfp4Error", "lib", "library_path",
     "rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
     "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
-    "rfp4_gemm_dequant", "MAX_GEMV_PARTS",
+    "rfp4_gemm_dequant", "rfp4_quantize", "RFP4_F32", "MAX_GEMV_PARTS",
 ]

@@ -15,6 +15,8 @@ namespace {
 
 constexpr int64_t kMaxDim = 2147483647;  // n, m, k <= 2^31 - 1
 static_assert(RFP4_MAX_GEMV_PARTS == rfp4::kMaxGemvParts, "parts limit of the header and the kernels");
+static_assert(RFP4_F16 == rfp4::kF16 && RFP4_BF16 == rfp4::kBF16 && RFP4_F32 == rfp4::kF32,
+              "dtype codes of the header and the kernels");
 constexpr int64_t kMaxElems = int64_t(1) << 39;  // elements of A or C (2^40 bytes of bf16)
 
 bool layout_ok(int layout) { return layout == RFP4_DUAL || layout == RFP4_FAST; }
@@ -172,6 +174,21 @@ rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const voi
                                     static_cast<const uint16_t*>(a), m, lda,
                                     static_cast<uint16_t*>(c), ldc,
                                     static_cast<hipStream_t>(stream)));
+}
+
+rfp4_status rfp4_quantize(const void* src, int src_dtype, int64_t n, int64_t k, int64_t lds,
+                          int layout, void* w_out, void* stream) {
+  if (!layout_ok(layout)) return RFP4_ERR_UNSUPPORTED;
+  if (src_dtype != RFP4_F32 && src_dtype != RFP4_BF16 && src_dtype != RFP4_F16)
+    return RFP4_ERR_UNSUPPORTED;
+  if (n < 1 || n > kMaxDim || k < 32 || k > kMaxDim || (k % 32) != 0) return RFP4_ERR_SHAPE;
+  if (lds < k || lds > kMaxElems / n) return RFP4_ERR_SHAPE;
+  if (src == nullptr || w_out == nullptr) return RFP4_ERR_NULL;
+  const int64_t esize = src_dtype == RFP4_F32 ? 4 : 2;
+  if (!aligned16(src) || !aligned16(w_out) || (lds * esize) % 16 != 0) return RFP4_ERR_UNSUPPORTED;
+  return from_hip(rfp4::launch_quantize(src, src_dtype, n, k, lds, layout,
+                                        static_cast<uint8_t*>(w_out),
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -13,6 +13,7 @@ constexpr int kDual = 0;
 constexpr int kFast = 1;
 constexpr int kF16 = 0;
 constexpr int kBF16 = 1;
+constexpr int kF32 = 2;
 
 // Bytes per 32-weight block ("Block Layout": qs[16] then e[2] or e).
 constexpr int block_bytes(int layout) { return layout == kDual ? 18 : 17; }
@@ -24,6 +25,10 @@ int device_cu_count();
 // 16-byte aligned, pointers non-null and aligned as the public header requires.
 hipError_t launch_dequant(const uint8_t* w, int layout, int64_t n, int64_t k, float* out,
                           int64_t ldo, hipStream_t stream);
+// Encoder: n rows of k values (row stride lds elements, dtype kF32 / kBF16 / kF16)
+// -> n * k / 32 packed blocks, back to back from `out` (16-byte aligned).
+hipError_t launch_quantize(const void* src, int dtype, int64_t n, int64_t k, int64_t lds,
+                           int layout, uint8_t* out, hipStream_t stream);
 hipError_t launch_dequant_bf16(const uint8_t* w, int layout, int64_t n, int64_t k, uint16_t* out,
                                int64_t ldo, hipStream_t stream);
 

@@ -14,7 +14,11 @@ Recipe (every workload, seed fixed per workload):
   replacement, get every index in {7, 15} (magnitude 10, random sign) and scale
   (15 << 3) | M with M uniform in 0..6 (the largest finite exponent);
 * activations: standard normal float32, rounded to nearest even into fp16 (NumPy) or
-  bf16 (torch).
+  bf16 (torch);
+* real-valued weights (quantizer input): standard normal times a per-row scale
+  0.02 * exp(N(0, 0.5^2)), with 0.1 % of the entries (drawn without replacement)
+  multiplied by 20 as outliers, in float32, then rounded to nearest even into bf16
+  or fp16 where asked.
 
 Draw order per workload: index bytes, scale bytes, stress choice, activations.
 """
@@ -69,6 +73,24 @@ def activations(rng: np.random.Generator, rows: int, k: int, dtype: str):
         return torch.from_numpy(x.astype(np.float16))
     if dtype == "bf16":
         return torch.from_numpy(x).to(torch.bfloat16)
+    raise ValueError(dtype)
+
+
+def real_weights(rng: np.random.Generator, n: int, k: int, dtype: str):
+    """(n, k) real-valued weights as a CPU torch tensor of dtype 'f32', 'bf16' or 'f16'."""
+    import torch
+
+    row = 0.02 * np.exp(0.5 * rng.standard_normal(size=(n, 1), dtype=np.float32))
+    v = rng.standard_normal(size=(n, k), dtype=np.float32) * row.astype(np.float32)
+    pick = rng.choice(n * k, size=(n * k) // 1000, replace=False)
+    v.reshape(-1)[pick] *= np.float32(20.0)
+    t = torch.from_numpy(v)
+    if dtype == "f32":
+        return t
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    if dtype == "f16":
+        return t.to(torch.float16)
     raise ValueError(dtype)
 
 

@@ -184,6 +184,22 @@ def test_gemm_argument_errors(L):
     assert f(P, 0, 64, 96, P2, 16, 96, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED
 
 
+def test_quantize_argument_errors(L):
+    f = L.rfp4_quantize
+    assert f(P, 3, 4, 64, 64, 0, P2, NULL) == R.RFP4_ERR_UNSUPPORTED  # dtype
+    assert f(P, R.RFP4_BF16, 4, 64, 64, 2, P2, NULL) == R.RFP4_ERR_UNSUPPORTED  # layout
+    assert f(P, R.RFP4_BF16, 0, 64, 64, 0, P2, NULL) == R.RFP4_ERR_SHAPE  # n = 0
+    assert f(P, R.RFP4_BF16, 4, 48, 48, 0, P2, NULL) == R.RFP4_ERR_SHAPE  # k % 32
+    assert f(P, R.RFP4_BF16, 4, 64, 56, 0, P2, NULL) == R.RFP4_ERR_SHAPE  # lds < k
+    assert f(P, R.RFP4_BF16, 1 << 20, 64, 1 << 20, 0, P2, NULL) == R.RFP4_ERR_SHAPE  # n * lds > 2^39
+    assert f(NULL, R.RFP4_BF16, 4, 64, 64, 0, P2, NULL) == R.RFP4_ERR_NULL
+    assert f(P, R.RFP4_BF16, 4, 64, 64, 0, NULL, NULL) == R.RFP4_ERR_NULL
+    assert f(UNALIGNED, R.RFP4_BF16, 4, 64, 64, 0, P2, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, R.RFP4_BF16, 4, 64, 64, 0, UNALIGNED, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, R.RFP4_BF16, 4, 64, 68, 0, P2, NULL) == R.RFP4_ERR_UNSUPPORTED  # 136-byte rows
+    assert f(P, R.RFP4_F32, 4, 64, 66, 1, P2, NULL) == R.RFP4_ERR_UNSUPPORTED  # 264-byte rows
+
+
 def test_validate_null_and_shape(L):
     bad = ctypes.c_int64(123)
     assert L.rfp4_validate(NULL, 0, 1, 32, ctypes.byref(bad)) == R.RFP4_ERR_NULL

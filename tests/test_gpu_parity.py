@@ -484,3 +484,100 @@ def test_gemm_full_size_sampled():
     c_ref, den = O.gemm_rows(w, cfg["layout"], n, k, x64(a), cols)
     assert gemm_error(c[:, cols], c_ref, den) <= TOL
     assert np.all(np.isfinite(c))
+
+
+# ------------------------------------------------------------------ quantize
+
+QDT = {"f32": (torch.float32, R.RFP4_F32), "bf16": (torch.bfloat16, R.RFP4_BF16),
+       "f16": (torch.float16, R.RFP4_F16)}
+
+
+def run_quantize(src, layout, lds=None):
+    """rfp4_quantize on a CPU tensor (n, k); columns k..lds-1 of a padded source hold
+    NaN (a read past k would saturate its group). Returns uint8 (n, row_bytes)."""
+    n, k = src.shape
+    code = {torch.float32: R.RFP4_F32, torch.bfloat16: R.RFP4_BF16, torch.float16: R.RFP4_F16}[src.dtype]
+    lds = k if lds is None else lds
+    sd = torch.full((n, lds), float("nan"), dtype=src.dtype, device=DEV)
+    sd[:, :k] = src.to(DEV)
+    rb = synth.row_bytes(layout, k)
+    out = torch.full((n * rb + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    st = R.lib().rfp4_quantize(R._ptr(sd), code, n, k, lds, layout, R._ptr(out), R._stream(None))
+    assert st == R.RFP4_OK, R.rfp4_status_string(st)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[n * rb:] == 0xA5), "quantize wrote past its output"
+    return o[: n * rb].reshape(n, rb)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("shape", [(37, 800), (1, 32), (5, 96), (300, 544)], ids=lambda s: "n{}k{}".format(*s))
+def test_quantize_matches_oracle(shape, layout, dt):
+    """Byte-exact against the oracle; (37, 800) spans several 256-block segments and
+    ends on a partial one whose byte count is not a multiple of 16."""
+    n, k = shape
+    src = synth.real_weights(np.random.default_rng(n * 7 + k), n, k, dt)
+    got = run_quantize(src, layout)
+    assert np.array_equal(got, O.quantize(x64(src), layout))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_quantize_padded_rows(layout, dt):
+    n, k, lds = 33, 256, 264
+    src = synth.real_weights(np.random.default_rng(5), n, k, dt)
+    assert np.array_equal(run_quantize(src, layout, lds), O.quantize(x64(src), layout))
+
+
+def quantize_edge_rows(dt):
+    """Rows of 128 values: zeros and negative zeros; NaN and infinities; saturation;
+    exact ties at a normal and a subnormal scale; tiny values; mixed magnitudes."""
+    big = {"f32": 3e38, "bf16": 3e38, "f16": 60000.0}[dt]
+    tiny = {"f32": 1e-30, "bf16": 1e-30, "f16": 6e-8}[dt]
+    rows = np.zeros((8, 128), dtype=np.float64)
+    rows[0, 3] = -0.0
+    rows[0, 40:48] = -0.0
+    rows[1, 0] = np.nan
+    rows[1, 5] = 1.0
+    rows[1, 20] = np.inf
+    rows[1, 40] = -np.inf
+    rows[1, 41] = -3.0
+    rows[1, 70] = np.nan
+    rows[1, 71] = -np.inf
+    rows[2, :32] = big
+    rows[2, 32:64] = -big * np.linspace(0, 1, 32)
+    ties = np.array([0.5, 1.5, 2.5, 3.5, 5.0, 7.0, 9.0, 10.0, 0.25, 4.0, 6.0, 8.0, 1.0, 2.0, 3.0, 9.5])
+    s_norm = 0.5 * 1.375 * 2.0 ** -1   # decoded scale of byte 0x33
+    s_sub = 5 * 2.0 ** -10              # decoded scale of byte 0x05
+    rows[3] = np.concatenate([ties, -ties, ties[::-1], -ties[::-1]] * 2) * s_norm
+    rows[4] = np.concatenate([ties, -ties, ties[::-1], -ties[::-1]] * 2) * s_sub
+    rows[5] = tiny * np.arange(128) * (-1.0) ** np.arange(128)
+    rows[6] = np.exp2(np.arange(128) % 30 - 15.0) * (-1.0) ** (np.arange(128) // 3)
+    rows[7, ::16] = 2240.0  # 10 * S(126), the largest finite reach
+    rows[7, 1::16] = 2240.0 * (1 + 2.0 ** -10)
+    t = torch.from_numpy(rows).to(QDT[dt][0])
+    return t
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_quantize_edge_cases(layout, dt):
+    src = quantize_edge_rows(dt)
+    got = run_quantize(src, layout)
+    ref = O.quantize(x64(src), layout)
+    assert np.array_equal(got, ref)
+    sb = got.reshape(8, 4, synth.block_bytes(layout))[:, :, 16:]
+    assert np.all(sb <= 126)
+    assert np.all(got[0] == 0)
+
+
+@pytest.mark.parametrize("layout,dt", [(0, "bf16"), (1, "f32"), (0, "f16")])
+def test_quantize_full_size_sampled(layout, dt):
+    """The up-projection shape (17408 x 5120) in one launch; rows are independent, so
+    the oracle checks a seeded sample of rows plus the first and last."""
+    n, k = 17408, 5120
+    src = synth.real_weights(np.random.default_rng(3), n, k, dt)
+    got = run_quantize(src, layout)
+    rows = np.unique(np.concatenate([np.random.default_rng(4).choice(n, 48, replace=False), [0, n - 1]]))
+    assert np.array_equal(got[rows], O.quantize(x64(src[rows]), layout))
