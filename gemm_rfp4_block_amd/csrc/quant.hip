@@ -36,44 +36,99 @@ constexpr int kPasses = 4;                              // blocks per 4-thread t
 constexpr int kSeg = kQuantThreads / 4 * kPasses;       // blocks per workgroup segment
 constexpr int kMaxSegBytes = kSeg * 18;
 
-// Smallest b in 0..126 with 10 * S(b) >= a, where a is the magnitude's bit pattern
-// (NaN patterns compare above every finite value and infinity, so they saturate).
-// Lower-bound search over the 127 candidates: lo ends at the number of bytes that do
-// not reach (127 when none does, hence the clamp to the saturation byte).
-__device__ __forceinline__ uint32_t scale_byte_for(uint32_t amax_bits) {
-  uint32_t lo = 0, hi = 127;
-#pragma unroll
-  for (int it = 0; it < 7; ++it) {  // 2^7 >= 127 + 1 outcomes
-    const uint32_t mid = (lo + hi) >> 1;
-    const bool reach = __float_as_uint(10.0f * scale_exact(mid)) >= amax_bits;
-    hi = reach ? mid : hi;
-    lo = reach ? lo : mid + 1;
+// Scale of a group: the smallest b in 0..126 whose decoded scale S(b) has
+// 10 * S(b) >= amax, with amax given by its fp32 bit pattern (NaN patterns compare
+// above every finite value and infinity, so they saturate at b = 126).
+// r = fl(fl(0.1 * amax) * (1 - 2^-20)) is at most amax / 10 and within a relative
+// 2^-19 of it, far closer than the relative spacing of the decoded scales (>= 1/16),
+// so the smallest decoded scale >= r is the answer or the one below it, and one exact
+// comparison settles which. Decoded scales below 2^-7 are b * 2^-10; from 2^-7 up
+// they are the fp32 values with three mantissa bits, whose bit patterns give b
+// directly (fp32 exponent bias 127 against 7 + 1 for the halved E4M3 value).
+struct GroupScale {
+  float s;     // S(b)
+  uint32_t b;  // scale byte
+};
+
+__device__ __forceinline__ GroupScale group_scale(uint32_t amax_bits) {
+  constexpr uint32_t kReach126 = 0x450C0000u;  // bits of 10 * S(126) = 2240
+  const float q = __uint_as_float(amax_bits);
+  const float r = (q * 0.1f) * (1.0f - 0x1p-20f);
+  const bool small = r < 0x1p-7f;
+  const float s_small = __builtin_ceilf(r * 1024.0f) * 0x1p-10f;
+  const float s_large = __uint_as_float((__float_as_uint(r) + 0xFFFFFu) & 0xFFF00000u);
+  float s = small ? s_small : s_large;
+  const float step = small ? 0x1p-10f : __uint_as_float(__float_as_uint(s) & 0x7F800000u) * 0.125f;
+  s = (10.0f * s < q) ? s + step : s;
+  uint32_t b = s < 0x1p-7f ? static_cast<uint32_t>(s * 1024.0f) : (__float_as_uint(s) >> 20) - 952u;
+  if (amax_bits > kReach126) {
+    s = 224.0f;
+    b = 126;
   }
-  return min(lo, 126u);
+  return {s, b};
 }
 
-// Eight consecutive source values as fp32 (exact widening).
+// Keeps a value in a register as computed (stops the compiler from rewriting a
+// select between two products as a product of a select, which costs a multiply per
+// weight).
+__device__ __forceinline__ float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Lane exchange inside groups of four lanes (DPP quad permutations).
+template <int XOR>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t v) {
+  constexpr int ctrl = XOR == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] and [2,3,0,1]
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), ctrl, 0xF, 0xF, false));
+}
+
+// Eight consecutive source values of one thread: raw words plus helpers.
 template <int DT>
-__device__ __forceinline__ void widen8(const uint4 r0, const uint4 r1, float (&f)[8]) {
-  if constexpr (DT == kF32) {
-    const uint32_t d[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+struct Eight {
+  uint32_t d[DT == kF32 ? 8 : 4];
+
+  __device__ __forceinline__ float value(int i) const {
+    if constexpr (DT == kF32) return __uint_as_float(d[i]);
+    else if constexpr (DT == kBF16)
+      return __uint_as_float((i & 1) ? (d[i >> 1] & 0xFFFF0000u) : (d[i >> 1] << 16));
+    else
+      return static_cast<float>(
+          __builtin_bit_cast(_Float16, static_cast<uint16_t>(d[i >> 1] >> (16 * (i & 1)))));
+  }
+
+  // Largest magnitude as an fp32 bit pattern (integer maximum of the magnitude bits,
+  // which orders non-negative values and puts NaN above infinity).
+  __device__ __forceinline__ uint32_t amax_bits() const {
+    if constexpr (DT == kF32) {
+      uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(d[i]);
-  } else {
-    const uint32_t d[4] = {r0.x, r0.y, r0.z, r0.w};
+      for (int i = 0; i < 8; ++i) m = max(m, d[i] & 0x7FFFFFFFu);
+      return m;
+    } else {
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == kBF16) {
-        f[2 * i] = __uint_as_float(d[i] << 16);
-        f[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
-      } else {
-        f[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(d[i])));
-        f[2 * i + 1] =
-            static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(d[i] >> 16)));
+      for (int i = 0; i < 4; ++i) {
+        lo = max(lo, d[i] & 0x7FFFu);
+        hi = max(hi, (d[i] >> 16) & 0x7FFFu);
       }
+      const uint32_t m = max(lo, hi);
+      if constexpr (DT == kBF16) return m << 16;
+      return __float_as_uint(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(m))));
     }
   }
-}
+
+  // Sign bits of values 4h .. 4h+3 at bit 7 of bytes 0..3.
+  __device__ __forceinline__ uint32_t signs(int h) const {
+    if constexpr (DT == kF32) {
+      const uint32_t a = __builtin_amdgcn_perm(d[4 * h + 1], d[4 * h], 0x0C0C0703u);
+      const uint32_t b = __builtin_amdgcn_perm(d[4 * h + 3], d[4 * h + 2], 0x07030C0Cu);
+      return a | b;
+    } else {
+      return __builtin_amdgcn_perm(d[2 * h + 1], d[2 * h], 0x07050301u);
+    }
+  }
+};
 
 template <int LAYOUT, int DT>
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint8_t* __restrict__ src,
@@ -83,62 +138,80 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint8_t* __r
                                                               uint8_t* __restrict__ out) {
   constexpr int BB = block_bytes(LAYOUT);
   constexpr int ESIZE = DT == kF32 ? 4 : 2;
+  constexpr int WORDS = DT == kF32 ? 8 : 4;
   __shared__ __attribute__((aligned(16))) uint8_t seg_buf[kMaxSegBytes];
 
   const int tid = threadIdx.x;
-  const int s = tid & 3;     // thread within its block's team
+  const int s = tid & 3;      // thread within its block's team
   const int team = tid >> 2;  // 0 .. 63
+  const uint32_t nb32 = static_cast<uint32_t>(nb);  // nb < 2^26
 
   for (int64_t seg = blockIdx.x; seg < segments; seg += gridDim.x) {
     const int64_t first = seg * kSeg;
-    // Row and block column of this team's first block; later passes add 64 blocks.
-    const int64_t gb0 = first + team;
-    const int64_t row0 = gb0 / nb;
-    const int64_t j0 = gb0 - row0 * nb;
+    const int64_t row_f = first / nb;  // uniform over the workgroup
+    const uint32_t j_f = static_cast<uint32_t>(first - row_f * nb);
 
-    uint4 ra[kPasses], rb[kPasses];  // rb: second 16 bytes (fp32 only)
+    Eight<DT> v[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-      ra[p] = rb[p] = uint4{0, 0, 0, 0};
-      if (gb0 + 64 * p < total_blocks) {
-        // j0 < nb < 2^26: the column of a later pass fits 32-bit division.
-        const uint32_t jj = static_cast<uint32_t>(j0) + 64u * p;
-        const uint32_t nb32 = static_cast<uint32_t>(nb);
-        const int64_t row = row0 + jj / nb32;
-        const int64_t j = jj % nb32;
-        const uint8_t* q = src + row * lds_bytes + (j * 32 + 8 * s) * ESIZE;
-        ra[p] = *reinterpret_cast<const uint4*>(q);
-        if constexpr (DT == kF32) rb[p] = *reinterpret_cast<const uint4*>(q + 16);
+#pragma unroll
+      for (int i = 0; i < WORDS; ++i) v[p].d[i] = 0;
+      if (first + team + 64 * p < total_blocks) {
+        // Block column j_f + team + 64p (< nb + 256) split into row and column.
+        uint32_t jj = j_f + team + 64u * p;
+        int64_t row = row_f;
+        if (nb32 >= 256) {  // at most one wrap
+          const bool wrap = jj >= nb32;
+          jj -= wrap ? nb32 : 0u;
+          row += wrap;
+        } else {
+          row += jj / nb32;
+          jj %= nb32;
+        }
+        const uint8_t* q = src + row * lds_bytes + (static_cast<int64_t>(jj) * 32 + 8 * s) * ESIZE;
+        const uint4 a = *reinterpret_cast<const uint4*>(q);
+        v[p].d[0] = a.x; v[p].d[1] = a.y; v[p].d[2] = a.z; v[p].d[3] = a.w;
+        if constexpr (DT == kF32) {
+          const uint4 b = *reinterpret_cast<const uint4*>(q + 16);
+          v[p].d[4] = b.x; v[p].d[5] = b.y; v[p].d[6] = b.z; v[p].d[7] = b.w;
+        }
       }
     }
 
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-      float f[8];
-      widen8<DT>(ra[p], rb[p], f);
-      uint32_t amax = 0;
+      uint32_t amax = v[p].amax_bits();
+      amax = max(amax, quad_xor<1>(amax));
+      if constexpr (LAYOUT == kFast) amax = max(amax, quad_xor<2>(amax));
+      const GroupScale g = group_scale(amax);
+      const uint32_t b = g.b;
+      // Midpoints between consecutive codebook magnitudes, times the scale (exact).
+      const float t0 = opaque(0.5f * g.s), t1 = opaque(1.5f * g.s), t2 = opaque(2.5f * g.s);
+      const float t3 = opaque(3.5f * g.s), t4 = opaque(5.0f * g.s), t5 = opaque(7.0f * g.s);
+      const float t6 = opaque(9.0f * g.s);
+      uint32_t codes[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = max(amax, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-      amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1)));
-      if constexpr (LAYOUT == kFast)
-        amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2)));
-      const uint32_t b = scale_byte_for(amax);
-      const float sc = scale_exact(b);
-      const float t0 = 0.5f * sc, t1 = 1.5f * sc, t2 = 2.5f * sc, t3 = 3.5f * sc;
-      const float t4 = 5.0f * sc, t5 = 7.0f * sc, t6 = 9.0f * sc;
-      uint32_t codes[2] = {0, 0};
+      for (int h = 0; h < 2; ++h) {
+        uint32_t mag = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float a = __builtin_fabsf(f[i]);
-        const uint32_t mag = (a > t0) + (a > t1) + (a > t2) + (a > t3) + (a > t4) + (a > t5) +
-                             (a > t6);
-        const uint32_t neg = (__float_as_uint(f[i]) >> 31) & (mag != 0);
-        codes[i >> 2] |= (mag | (neg << 3)) << (8 * (i & 3));
+        for (int i = 0; i < 4; ++i) {
+          // Number of midpoints below |w| by a three-level search; every comparison
+          // with NaN is false, so NaN gets magnitude 0.
+          const float a = __builtin_fabsf(v[p].value(4 * h + i));
+          const bool c1 = a > t3;
+          const bool c2 = a > (c1 ? t5 : t1);
+          const bool c3 = a > (c1 ? (c2 ? t6 : t4) : (c2 ? t2 : t0));
+          mag |= ((c1 ? 4u : 0u) | (c2 ? 2u : 0u) | (c3 ? 1u : 0u)) << (8 * i);
+        }
+        // Sign (index bit 3) only where the magnitude is non-zero: bytes are <= 7, so
+        // adding 7 sets bit 3 exactly for the non-zero ones.
+        const uint32_t nonzero = (mag + 0x07070707u) & 0x08080808u;
+        codes[h] = mag | ((v[p].signs(h) >> 4) & nonzero);
       }
       // Threads 0, 1 hold weights 0..15 (low nibbles), threads 2, 3 weights 16..31.
-      const uint32_t hi0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(codes[0]), 2));
-      const uint32_t hi1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(codes[1]), 2));
-      if (gb0 + 64 * p < total_blocks) {
+      const uint32_t hi0 = quad_xor<2>(codes[0]);
+      const uint32_t hi1 = quad_xor<2>(codes[1]);
+      if (first + team + 64 * p < total_blocks) {
         uint8_t* d = seg_buf + (64 * p + team) * BB;
         if (s < 2) {
           const uint32_t q0 = codes[0] | (hi0 << 4);
