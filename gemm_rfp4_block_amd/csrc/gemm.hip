@@ -268,12 +268,12 @@ __device__ __forceinline__ void decode_part(const BlockRaw& b, const uint4* tabs
 
 // Workgroup b computes tile t = b mod tiles, i.e. (t mod m_tiles, t / m_tiles), of the
 // region of C whose columns start at n_base, over the part b / tiles of `splits`
-// equal, even-length ranges of the k steps (k / 64 of them, an even number, at least
-// 2 * splits). With one split the tile is rounded to bf16 and stored; with more, the
+// equal, even-length ranges of the k steps (k / 64 of them, rounded up to an even
+// number, at least 2 * splits; KT marks k % 128 != 0). With one split the tile is rounded to bf16 and stored; with more, the
 // fp32 accumulators go to partial[b] (BM x BN floats in accumulator order) for
 // gemm_reduce_kernel. Rows and columns outside [0, m) x [0, n) are computed on clamped
 // inputs and never stored.
-template <int LAYOUT, typename Cfg>
+template <int LAYOUT, typename Cfg, bool KT>
 __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __restrict__ w,
                                                              int n, int nb,
                                                              const uint16_t* __restrict__ a,
@@ -300,7 +300,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
   const int m0 = (tile_id % m_tiles) * Cfg::BM;
   const int64_t n0 = n_base + static_cast<int64_t>(tile_id / m_tiles) * Cfg::BN;
   const int64_t rowbytes = static_cast<int64_t>(nb) * BB;
-  const int half_steps = nb / 4;  // BK = 64 = two blocks; steps come in pairs
+  // BK = 64 = two blocks; steps come in pairs. With KT (k tail: nb not a multiple of
+  // four) the last pair reaches past k, and its A chunks and weight blocks beyond k
+  // are read as zeros.
+  const int half_steps = KT ? (nb + 3) / 4 : nb / 4;
   const int s_begin = 2 * static_cast<int>(static_cast<int64_t>(split) * half_steps / splits);
   const int s_end = 2 * static_cast<int>(static_cast<int64_t>(split + 1) * half_steps / splits);
   const int s_last = s_end - 1;
@@ -321,8 +324,19 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
     a_p[i] = a + a_chunk * 8 + min(m0 + a_row0 + Cfg::kARows * i, m - 1) * lda;
   auto load_a = [&](int s) {
     AChunks r;
+    if constexpr (KT) {
+      // Past k: load column 0 of the row instead (always in bounds) and zero the chunk.
+      const bool ok = s * BK + a_chunk * 8 < nb * 32;
+      const int off = ok ? s * BK : -a_chunk * 8;
 #pragma unroll
-    for (int i = 0; i < AP; ++i) r.v[i] = *reinterpret_cast<const uint4*>(a_p[i] + s * BK);
+      for (int i = 0; i < AP; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(a_p[i] + off);
+        r.v[i] = ok ? v : uint4{0u, 0u, 0u, 0u};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < AP; ++i) r.v[i] = *reinterpret_cast<const uint4*>(a_p[i] + s * BK);
+    }
     return r;
   };
   char* const a_st = smem + a_row0 * 128 + (swz_chunk(a_row0, a_chunk) << 4);
@@ -359,7 +373,18 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
   auto load_w = [&](int s) {
     WRaw r;
 #pragma unroll
-    for (int q = 0; q < BP; ++q) r.b[q] = load_block<LAYOUT>(w_row[q] + s * 2 * BB);
+    for (int q = 0; q < BP; ++q) {
+      if constexpr (KT) {
+        // Past k: load the row's first block instead and zero it (index 0, scale 0).
+        const int blk = (w_idx + Cfg::kThreads * q) & 1;
+        const bool ok = 2 * s + blk < nb;
+        const BlockRaw b = load_block<LAYOUT>(w_row[q] + (ok ? s * 2 * BB : -blk * BB));
+        r.b[q].qs = ok ? b.qs : uint4{0u, 0u, 0u, 0u};
+        r.b[q].sc = ok ? b.sc : 0u;
+      } else {
+        r.b[q] = load_block<LAYOUT>(w_row[q] + s * 2 * BB);
+      }
+    }
     return r;
   };
   // Decode tables of the scale bytes of this thread's blocks (entries e0, e1).
@@ -725,10 +750,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
     if (row0 + q < m) c[(row0 + q) * ldc + gn] = bf16_rne(v[q]);
 }
 
-template <typename Cfg>
+template <typename Cfg, bool KT>
 const void* kernel_ptr(int layout) {
-  return layout == kDual ? reinterpret_cast<const void*>(&gemm_kernel<kDual, Cfg>)
-                         : reinterpret_cast<const void*>(&gemm_kernel<kFast, Cfg>);
+  return layout == kDual ? reinterpret_cast<const void*>(&gemm_kernel<kDual, Cfg, KT>)
+                         : reinterpret_cast<const void*>(&gemm_kernel<kFast, Cfg, KT>);
 }
 
 // Raises the dynamic-LDS limit of both configurations once per device; threads that
@@ -740,12 +765,13 @@ hipError_t ensure_attributes(int layout) {
   if (e != hipSuccess) return e;
   const bool cached = dev >= 0 && dev < 64;
   if (cached && done[dev][layout].load(std::memory_order_acquire)) return hipSuccess;
-  e = hipFuncSetAttribute(kernel_ptr<MainCfg>(layout), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          MainCfg::kLdsBytes);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(kernel_ptr<TailCfg>(layout), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          TailCfg::kLdsBytes);
-  if (e != hipSuccess) return e;
+  const void* fns[4] = {kernel_ptr<MainCfg, false>(layout), kernel_ptr<MainCfg, true>(layout),
+                        kernel_ptr<TailCfg, false>(layout), kernel_ptr<TailCfg, true>(layout)};
+  const int lds[4] = {MainCfg::kLdsBytes, MainCfg::kLdsBytes, TailCfg::kLdsBytes, TailCfg::kLdsBytes};
+  for (int i = 0; i < 4; ++i) {
+    e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
+    if (e != hipSuccess) return e;
+  }
   if (cached) done[dev][layout].store(true, std::memory_order_release);
   return hipSuccess;
 }
@@ -763,12 +789,16 @@ hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint
   const int tiles = static_cast<int>(m_tiles * n_tiles);
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(tiles) * splits));
   float* part = splits > 1 ? partial : nullptr;
-  if (layout == kDual)
-    gemm_kernel<kDual, Cfg><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>(
-        w, n, nb, a, m, lda, c, ldc, m_tiles, tiles, n_base, splits, part);
-  else
-    gemm_kernel<kFast, Cfg><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>(
-        w, n, nb, a, m, lda, c, ldc, m_tiles, tiles, n_base, splits, part);
+#define RFP4_GEMM_LAUNCH(L, KT)                                                     \
+  gemm_kernel<L, Cfg, KT><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>( \
+      w, n, nb, a, m, lda, c, ldc, m_tiles, tiles, n_base, splits, part)
+  const bool kt = nb % 4 != 0;
+  if (layout == kDual) {
+    if (kt) RFP4_GEMM_LAUNCH(kDual, true); else RFP4_GEMM_LAUNCH(kDual, false);
+  } else {
+    if (kt) RFP4_GEMM_LAUNCH(kFast, true); else RFP4_GEMM_LAUNCH(kFast, false);
+  }
+#undef RFP4_GEMM_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t groups = static_cast<int64_t>(tiles) * (Cfg::BM * Cfg::BN / 4);
@@ -800,7 +830,7 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
     const int64_t cols = n - (strips - t) * MainCfg::BN;
     return t > 0 ? slabs * ((cols + TailCfg::BN - 1) / TailCfg::BN) : 0;
   };
-  const int max_split = nb / 4;  // each split needs at least two 64-column steps
+  const int max_split = (nb + 3) / 4;  // each split needs at least two 64-column steps
   const char* env = getenv("RFP4_GEMM_PLAN");
   const std::string plan = env != nullptr ? env : "";
   if (plan == "main") return Plan{0, 1, 0};
@@ -883,10 +913,9 @@ hipError_t split_workspace(hipStream_t stream, size_t bytes, float** out) {
 
 hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
                        int64_t m, int64_t lda, uint16_t* c, int64_t ldc, hipStream_t stream) {
+  // Any k % 32 == 0: the kernel runs two 64-column steps per iteration, and when
+  // k % 128 != 0 its k-tail variant zero-fills the last pair past k.
   const int nb = static_cast<int>(k / 32);
-  // The kernel runs two 64-column steps per iteration; rows of whole 16-byte multiples
-  // (checked by the API) give k % 256 == 0.
-  if (nb % 4 != 0) return hipErrorInvalidValue;
   hipError_t e = ensure_attributes(layout);
   if (e != hipSuccess) return e;
   const int cus = device_cu_count();

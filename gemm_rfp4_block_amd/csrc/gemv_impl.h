@@ -88,8 +88,10 @@ struct UnitRaw {
 // blocks) start at 1-, 2- or 3-byte offsets. Such a unit is read with dword-aligned
 // loads from the word boundary below it and shifted into place per lane with
 // v_alignbyte_b32: unaligned 16-byte loads cost the memory pipeline measurably more.
-// The extra bytes read lie inside the row: rows hold a multiple of 8 (dual) or 16
-// (fast) blocks, so the last unit of a row ends on a word boundary.
+// The extra bytes read lie in the last word that holds a byte of the unit (dual units
+// and pairs of fast blocks start at even offsets, since their rows hold an even number
+// of bytes), so a read never reaches past the word of the matrix's last byte and never
+// crosses into another page.
 template <int LAYOUT, int P>
 __device__ __forceinline__ void load_unit_realigned(const uint8_t* p, UnitRaw<P>& u) {
   constexpr int NW = P == 1 ? 5 : 9;  // words covering the unit from its word boundary
@@ -141,6 +143,7 @@ __device__ __forceinline__ void load_unit(const uint8_t* p, UnitRaw<P>& u) {
     u.d[7] = v1.w;
     if constexpr (LAYOUT == kDual) {
       u.d[8] = load4(p + 32);  // 4-byte aligned: units start at multiples of 36 bytes
+                               // (P = 2 needs an even block count, so rows hold 36j bytes)
     } else {
       uint16_t t;
       __builtin_memcpy(&t, p + 32, 2);
@@ -545,6 +548,10 @@ hipError_t launch3(const GemvPart* parts, int count, int nb, const uint16_t* x, 
   // Activations from global memory: single blocks per unit (a forced P = 2 mapping keeps
   // its lane count).
   if (!xlds && pl.p == 2) pl = make_plan(1, pl.log2cl, parts, count, nb, waves_per_cu, threads);
+  // Per-lane row offsets are 32-bit: a forced mapping with several rows per wavefront
+  // falls back to one row per wavefront when the rows are too long for them.
+  if (static_cast<int64_t>((64 >> pl.log2cl) - 1) * nb * block_bytes(LAYOUT) >= (int64_t(1) << 31))
+    pl = make_plan(1, 6, parts, count, nb, waves_per_cu, threads);
   GemvParts<NP> gp;
   gp.count = count;
   gp.gbeg[0] = 0;

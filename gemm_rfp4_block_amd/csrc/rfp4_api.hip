@@ -24,12 +24,13 @@ bool layout_ok(int layout) { return layout == RFP4_DUAL || layout == RFP4_FAST; 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shape and alignment of the packed weight matrix, shared by every device entry point.
+// Rows may have any length (k % 32 == 0): the kernels read blocks at any byte offset.
 rfp4_status check_weights(const void* w, int layout, int64_t n, int64_t k) {
   if (!layout_ok(layout)) return RFP4_ERR_UNSUPPORTED;
   if (n < 1 || n > kMaxDim || k < 32 || k > kMaxDim || (k % 32) != 0) return RFP4_ERR_SHAPE;
   if (w == nullptr) return RFP4_ERR_NULL;
-  const int64_t row = (k / 32) * rfp4::block_bytes(layout);
-  if (!aligned16(w) || (row % 16) != 0) return RFP4_ERR_UNSUPPORTED;
+  if (n * (k / 32) * rfp4::block_bytes(layout) > (int64_t(1) << 40)) return RFP4_ERR_SHAPE;
+  if (!aligned16(w)) return RFP4_ERR_UNSUPPORTED;
   return RFP4_OK;
 }
 

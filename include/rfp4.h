@@ -34,12 +34,12 @@
  *   - Every argument check runs before any HIP call, so argument errors are
  *     reported without touching the GPU. Scale bytes are NOT checked on these hot
  *     paths: call rfp4_validate once when the weights are loaded.
- *   - Alignment: W must be 16-byte aligned and its rows must be a multiple of 16
- *     bytes long (dual: k % 256 == 0; fast: k % 512 == 0), otherwise
- *     RFP4_ERR_UNSUPPORTED. Activations and outputs must be 16-byte aligned with
- *     leading dimensions that keep every row 16-byte aligned.
- *   - Sizes: 1 <= n, m and 32 <= k, with n, m, k <= 2^31 - 1; buffers of up to
- *     2^40 bytes are addressed with 64-bit offsets.
+ *   - Alignment: W must start on a 16-byte boundary (RFP4_ERR_UNSUPPORTED
+ *     otherwise); its rows may have any length, so k is any multiple of 32 and rows
+ *     need not start on a 16-byte boundary. Activations and outputs must be 16-byte
+ *     aligned with leading dimensions that keep every row 16-byte aligned.
+ *   - Sizes: 1 <= n, m and 32 <= k, with n, m, k <= 2^31 - 1 and W at most 2^40
+ *     bytes (RFP4_ERR_SHAPE otherwise); buffers are addressed with 64-bit offsets.
  */
 #ifndef RFP4_H
 #define RFP4_H

@@ -83,8 +83,10 @@ def test_dequant_argument_errors(L):
     assert f(P, 0, 4, 500, P2, 512, NULL) == R.RFP4_ERR_SHAPE
     assert f(P, 0, 4, 0, P2, 512, NULL) == R.RFP4_ERR_SHAPE
     assert f(P, 0, 4, 512, P2, 511, NULL) == R.RFP4_ERR_SHAPE  # ldo < k
-    assert f(P, 0, 4, 96, P2, 96, NULL) == R.RFP4_ERR_UNSUPPORTED  # dual row not 16-B multiple
-    assert f(P, 1, 4, 256, P2, 256, NULL) == R.RFP4_ERR_UNSUPPORTED  # fast needs k % 512
+    # rows of any length are accepted (k = 96: 54-byte rows); the other checks still apply
+    assert f(P, 0, 4, 96, P2, 95, NULL) == R.RFP4_ERR_SHAPE  # ldo < k
+    assert f(UNALIGNED, 1, 4, 96, P2, 96, NULL) == R.RFP4_ERR_UNSUPPORTED  # W base
+    assert f(P, 0, 1 << 30, 1 << 20, P2, 1 << 20, NULL) == R.RFP4_ERR_SHAPE  # W > 2^40 bytes
     assert f(UNALIGNED, 0, 4, 512, P2, 512, NULL) == R.RFP4_ERR_UNSUPPORTED
     assert f(P, 0, 4, 512, UNALIGNED, 512, NULL) == R.RFP4_ERR_UNSUPPORTED
     assert f(P, 0, 4, 512, P2, 514, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldo % 4
@@ -106,7 +108,8 @@ def test_gemv_argument_errors(L):
     assert f(P, 0, 8, 512, P2, 0, 2, 516, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldx % 8
     assert f(P, 0, 8, 512, UNALIGNED, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
     assert f(P, 0, 8, 512, P2, 0, 1, 512, UNALIGNED, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
-    assert f(P, 1, 8, 768, P2, 0, 1, 768, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # fast k % 512
+    assert f(UNALIGNED, 1, 8, 96, P2, 0, 1, 96, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # W base
+    assert f(P, 1, 8, 96, P2, 0, 1, 95, P, 8, NULL) == R.RFP4_ERR_SHAPE  # ldx < k, 51-byte rows
 
 
 def test_gemv_multi_argument_errors(L):
@@ -181,7 +184,8 @@ def test_gemm_argument_errors(L):
     assert f(P, 0, 64, 512, P2, 16, 520, P, 68, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldc % 8
     assert f(P, 0, 64, 512, P2, 16, 516, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED  # lda % 8
     assert f(P, 4, 64, 512, P2, 16, 512, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED
-    assert f(P, 0, 64, 96, P2, 16, 96, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(UNALIGNED, 0, 64, 96, P2, 16, 96, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED  # W base
+    assert f(P, 0, 64, 96, P2, 16, 95, P, 64, NULL) == R.RFP4_ERR_SHAPE  # lda < k, 54-byte rows
 
 
 def test_quantize_argument_errors(L):

@@ -581,3 +581,133 @@ def test_quantize_full_size_sampled(layout, dt):
     got = run_quantize(src, layout)
     rows = np.unique(np.concatenate([np.random.default_rng(4).choice(n, 48, replace=False), [0, n - 1]]))
     assert np.array_equal(got[rows], O.quantize(x64(src[rows]), layout))
+
+
+# ------------------------------------------------------------------ rows of any length
+# k % 32 == 0 only: row lengths that are not multiples of 16 bytes (so rows start at
+# every byte offset), odd block counts (single-block GEMV units), block counts that are
+# not multiples of four (the GEMM's zero-filled k tail) and one-block rows.
+
+UNALIGNED_DQ = [(0, 37, 96), (1, 29, 96), (0, 5, 32), (1, 7, 32), (0, 33, 1408), (1, 31, 544),
+                (1, 19, 1056), (0, 3, 4000)]
+
+
+@pytest.mark.parametrize("case", UNALIGNED_DQ, ids=lambda c: "L{}n{}k{}".format(*c))
+def test_unaligned_rows_dequant_bitwise(case):
+    layout, n, k = case
+    w = synth.weights(np.random.default_rng(8000 + n + k), layout, n, k, stress_frac=0.05)
+    wd = dev(w)
+    ref = O.dequantize_f32(w, layout, n, k)
+    got = R.rfp4_dequant(wd, layout, n, k).cpu().numpy()
+    assert np.array_equal(bits(got), bits(ref))
+    out = torch.empty((n, (k + 7) // 8 * 8), dtype=torch.bfloat16, device=DEV)
+    R.rfp4_dequant_bf16(wd, layout, n, k, out)
+    torch.cuda.synchronize()
+    gb = out[:, :k].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(gb, bf16_bits_of(ref))
+
+
+UNALIGNED_GEMV = [  # layout, n, k, batch, dtype
+    (0, 257, 96, 1, "f16"), (1, 255, 96, 3, "bf16"), (0, 100, 1408, 1, "bf16"), (1, 99, 1056, 8, "f16"),
+    (1, 33, 32, 2, "bf16"), (0, 1, 32, 1, "f16"), (0, 300, 4000, 1, "bf16"), (1, 77, 4000, 2, "f16"),
+    (1, 130, 1088, 4, "bf16"), (0, 64, 100000, 1, "f16"), (1, 40, 99968, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", UNALIGNED_GEMV, ids=lambda c: "L{}n{}k{}b{}{}".format(*c))
+def test_unaligned_rows_gemv(case):
+    layout, n, k, batch, dt = case
+    rng = np.random.default_rng(8100 + n + k + batch)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    x = synth.activations(rng, batch, k, dt)
+    check_gemv(w, layout, n, k, x, ldy=n + 1)
+
+
+@pytest.mark.parametrize("plan", ["1:1", "1:4", "1:64", "2:2", "2:16"])
+@pytest.mark.parametrize("case", [(0, 70, 1408, 2, "f16"), (1, 61, 1088, 1, "bf16"), (1, 45, 1056, 3, "f16")],
+                         ids=lambda c: "L{}n{}k{}b{}{}".format(*c))
+def test_unaligned_rows_gemv_forced_plan(case, plan, monkeypatch):
+    """Every lane mapping on rows at all byte offsets (an odd block count ignores a
+    forced P = 2 and takes single-block units)."""
+    monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
+    layout, n, k, batch, dt = case
+    rng = np.random.default_rng(8200 + n + k)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    x = synth.activations(rng, batch, k, dt)
+    check_gemv(w, layout, n, k, x)
+
+
+def test_unaligned_rows_gemv_multi():
+    layout, ns, k, batch = 1, [33, 1, 70, 5], 1056, 2
+    rng = np.random.default_rng(8300)
+    ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
+    x = synth.activations(rng, batch, k, "bf16")
+    ys = R.rfp4_gemv_multi([dev(w) for w in ws], layout, ns, k, x.to(DEV).contiguous())
+    torch.cuda.synchronize()
+    for w, n, y in zip(ws, ns, ys):
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
+
+
+UNALIGNED_GEMM = [  # layout, m, n, k
+    (0, 100, 200, 96), (1, 77, 136, 160), (0, 257, 520, 1408), (1, 64, 300, 1056), (0, 1, 8, 32),
+    (1, 130, 129, 544), (0, 33, 64, 224),
+]
+
+
+@pytest.mark.parametrize("case", UNALIGNED_GEMM, ids=lambda c: "L{}m{}n{}k{}".format(*c))
+def test_unaligned_rows_gemm(case):
+    layout, m, n, k = case
+    rng = np.random.default_rng(8400 + m + n + k)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    a = synth.activations(rng, m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a, ldc=n + 8 - n % 8)
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c, c_ref, den) <= TOL
+
+
+@pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4"])
+@pytest.mark.parametrize("case", [(0, 100, 200, 96), (1, 130, 264, 544), (0, 257, 300, 1376)],
+                         ids=lambda c: "L{}m{}n{}k{}".format(*c))
+def test_unaligned_rows_gemm_forced_tile_size(case, plan, monkeypatch):
+    """The zero-filled k tail in each tile configuration and in every split part
+    (k = 544: 17 blocks, so four splits of the five step pairs)."""
+    monkeypatch.setenv("RFP4_GEMM_PLAN", plan)
+    layout, m, n, k = case
+    rng = np.random.default_rng(8500 + m + n + k)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    a = synth.activations(rng, m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a, ldc=(n + 7) // 8 * 8)
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c, c_ref, den) <= TOL
+
+
+def test_unaligned_rows_gemm_tail_ignores_values_past_k():
+    """A's columns past k are never used: NaN stored in the padding after each row
+    (lda > k) does not reach the output of the zero-filled k tail."""
+    layout, m, n, k = 0, 65, 96, 160
+    lda = k + 8
+    rng = np.random.default_rng(8600)
+    w = synth.weights(rng, layout, n, k)
+    a = synth.activations(rng, m, k, "bf16")
+    ad = torch.full((m, lda), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ad[:, :k] = a.to(DEV)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    st = R.lib().rfp4_gemm(R._ptr(dev(w)), layout, n, k, R._ptr(ad), m, lda, R._ptr(c), n, R._stream(None))
+    assert st == R.RFP4_OK
+    torch.cuda.synchronize()
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c.to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
+
+
+@pytest.mark.parametrize("case", [(0, 100, 200, 96), (1, 64, 296, 1056)], ids=lambda c: "L{}m{}n{}k{}".format(*c))
+def test_unaligned_rows_gemm_dequant(case):
+    layout, m, n, k = case
+    rng = np.random.default_rng(8700 + m + n + k)
+    w = synth.weights(rng, layout, n, k)
+    a = synth.activations(rng, m, k, "bf16")
+    wbuf = torch.empty((n, (k + 7) // 8 * 8), dtype=torch.bfloat16, device=DEV)
+    c = R.rfp4_gemm_dequant(dev(w), layout, n, k, a.to(DEV).contiguous(), wbuf=wbuf)
+    torch.cuda.synchronize()
+    c_ref, den = O.gemm(w, layout, n, k, x64(a))
+    assert gemm_error(c.to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
