@@ -45,11 +45,18 @@ namespace {
 
 // Workgroups of 256 threads, or 1024 when long activation rows are staged in LDS (the
 // staging is then shared by 16 wavefronts and two workgroups fit a CU).
-constexpr int kThreadsSmall = 256;
+#ifndef RFP4_GEMV_SMALL_THREADS
+#define RFP4_GEMV_SMALL_THREADS 256
+#endif
+constexpr int kThreadsSmall = RFP4_GEMV_SMALL_THREADS;
 constexpr int kThreadsLarge = 1024;
 constexpr int kXLdsBudget = 40 * 1024;
 constexpr int kXLdsBudgetLarge = 80 * 1024;
 
+// Tuning knob (no effect on results): weight units in flight per lane.
+#ifndef RFP4_GEMV_DEPTH
+#define RFP4_GEMV_DEPTH 3
+#endif
 // Tuning knob (no effect on results): resident wavefronts per CU the launch is sized for.
 #ifndef RFP4_GEMV_WAVES_PER_CU
 #define RFP4_GEMV_WAVES_PER_CU 24
@@ -75,6 +82,28 @@ struct Act<kBF16> {
     return __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2, x), acc, false);
   }
 };
+
+// High bytes of the f16 encodings of the magnitudes 0, 1, 2, 3 (low word, byte 0
+// first) and 4, 6, 8, 10 (high word); the low bytes are all zero.
+constexpr uint32_t kF16HiLo = 0x42403C00u;
+constexpr uint32_t kF16HiHi = 0x49484644u;
+
+// Four f16 high bytes (byte i = weight of the low / high nibble of byte i of q).
+__device__ __forceinline__ uint32_t f16_high_bytes_low(uint32_t q) {
+  const uint32_t mag = __builtin_amdgcn_perm(kF16HiHi, kF16HiLo, q & 0x07070707u);
+  return mag | ((q << 4) & 0x80808080u);
+}
+
+__device__ __forceinline__ uint32_t f16_high_bytes_high(uint32_t q) {
+  const uint32_t mag = __builtin_amdgcn_perm(kF16HiHi, kF16HiLo, (q >> 4) & 0x07070707u);
+  return mag | (q & 0x80808080u);
+}
+
+// f16 pair of weights 0, 1 (or 2, 3) from four high bytes: selector 0x0C gives a zero byte.
+__device__ __forceinline__ f16x2 spread_f16(uint32_t h, bool hi_pair) {
+  const uint32_t v = __builtin_amdgcn_perm(0u, h, hi_pair ? 0x030C020Cu : 0x010C000Cu);
+  return __builtin_bit_cast(f16x2, v);
+}
 
 // Raw bytes of one unit of P consecutive blocks (see the file comment), as words.
 //   P = 1: d[0..3] = index bytes, d[4] = the scale byte(s) in its low bytes.
@@ -197,12 +226,23 @@ __device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, XUnit xu
   pair wl[8], wh[8];  // first half (low nibbles), second half (high nibbles)
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = codes_low(q[d]);
-    const uint32_t hi = codes_high(q[d]);
-    wl[2 * d] = A::decode(lo, false);
-    wl[2 * d + 1] = A::decode(lo, true);
-    wh[2 * d] = A::decode(hi, false);
-    wh[2 * d + 1] = A::decode(hi, true);
+    if constexpr (XT == kF16) {
+      // Every codebook magnitude is an f16 value whose low byte is zero: look up the
+      // high bytes (sign in bit 7) and spread them into f16 pairs with zero low bytes.
+      const uint32_t lo = f16_high_bytes_low(q[d]);
+      const uint32_t hi = f16_high_bytes_high(q[d]);
+      wl[2 * d] = spread_f16(lo, false);
+      wl[2 * d + 1] = spread_f16(lo, true);
+      wh[2 * d] = spread_f16(hi, false);
+      wh[2 * d + 1] = spread_f16(hi, true);
+    } else {
+      const uint32_t lo = codes_low(q[d]);
+      const uint32_t hi = codes_high(q[d]);
+      wl[2 * d] = A::decode(lo, false);
+      wl[2 * d + 1] = A::decode(lo, true);
+      wh[2 * d] = A::decode(hi, false);
+      wh[2 * d + 1] = A::decode(hi, true);
+    }
   }
 #pragma unroll
   for (int b = 0; b < BATCH; ++b) {
@@ -336,47 +376,83 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
   };
   seek();
   int unit_off = 0;
+  auto advance = [&]() {
+    ++issued;
+    unit_off += unit_stride;
+    if (++li == iters) {
+      li = 0;
+      unit_off = 0;
+      lg += S;
+      if (single) {
+        gbase += S * group_stride;
+        lane_off = min(r_in, max(n0 - 1 - lg * rl, 0)) * static_cast<int>(rowbytes);
+      } else if (issued < total) {
+        seek();
+      }
+    }
+  };
   auto load_next = [&](UnitRaw<P>& buf) {
     if (issued < total) {
       const int col = RAGGED ? min(unit_off + c_off, last_off) : unit_off + c_off;
       load_unit<LAYOUT, P>(gbase + col + lane_off, buf);
-      ++issued;
-      unit_off += unit_stride;
-      if (++li == iters) {
-        li = 0;
-        unit_off = 0;
-        lg += S;
-        if (single) {
-          gbase += S * group_stride;
-          lane_off = min(r_in, max(n0 - 1 - lg * rl, 0)) * static_cast<int>(rowbytes);
-        } else if (issued < total) {
-          seek();
-        }
-      }
+      advance();
     }
   };
+  // The first units are issued unconditionally (straight-line loads let the compiler
+  // wait for exactly the loads it needs): a wavefront with no unit left loads the first
+  // unit of the launch instead (in bounds) and never consumes it.
+  auto load_first = [&](UnitRaw<P>& buf) {
+    const bool live = issued < total;  // wave-uniform
+    const int col = RAGGED ? min(unit_off + c_off, last_off) : unit_off + c_off;
+    load_unit<LAYOUT, P>(live ? gbase + col + lane_off : w0, buf);
+    if (live) advance();
+  };
 
-  // Three units in flight per lane: the first before the activations are staged (its
-  // latency overlaps theirs), the next two right after the barrier; each consumed unit
-  // is replaced by the next one, so decoding starts as soon as the first unit lands
-  // while the following ones stream in.
-  UnitRaw<P> r0, r1, r2;
-  load_next(r0);
-
+  // D units in flight per lane. With the activations staged in LDS, the first
+  // staging loads are issued before the weight units, so the LDS stores wait only for
+  // them (memory counters retire in issue order) while the weight loads stay in flight;
+  // each consumed unit is then replaced by the next one.
+  constexpr int D = RFP4_GEMV_DEPTH;
+  UnitRaw<P> rb[D];
   if constexpr (XLDS) {
     const int units = BATCH * 4 * nu * P;  // 16-byte activation units
-    for (int t = threadIdx.x; t < units; t += THREADS) {
+    auto src_of = [&](int t) {  // global address of activation unit t
       const int cc = t & 3;
       const int jb = t >> 2;  // block index over all activation rows
-      const int b = jb / (nu * P);
+      const int b = BATCH == 1 ? 0 : jb / (nu * P);
       const int j = jb - b * nu * P;
-      xs[xs_index<P>(b, j / P, nu, j % P, cc)] =
-          *reinterpret_cast<const uint4*>(x + b * ldx + 32 * j + 8 * cc);
-    }
+      return reinterpret_cast<const uint4*>(x + b * ldx + 32 * j + 8 * cc);
+    };
+    auto dst_of = [&](int t) {
+      const int cc = t & 3;
+      const int jb = t >> 2;
+      const int b = BATCH == 1 ? 0 : jb / (nu * P);
+      const int j = jb - b * nu * P;
+      return xs + xs_index<P>(b, j / P, nu, j % P, cc);
+    };
+    // Four chunks per thread and round; the loads are clamped, so every lane loads in
+    // bounds, and only the stores are masked.
+    auto stage = [&](int t0, bool first) {
+      const uint4 v0 = *src_of(min(t0, units - 1));
+      const uint4 v1 = *src_of(min(t0 + THREADS, units - 1));
+      const uint4 v2 = *src_of(min(t0 + 2 * THREADS, units - 1));
+      const uint4 v3 = *src_of(min(t0 + 3 * THREADS, units - 1));
+      if (first) {  // uniform: the first round of every thread
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_first(rb[d]);
+      }
+      if (t0 < units) *dst_of(t0) = v0;
+      if (t0 + THREADS < units) *dst_of(t0 + THREADS) = v1;
+      if (t0 + 2 * THREADS < units) *dst_of(t0 + 2 * THREADS) = v2;
+      if (t0 + 3 * THREADS < units) *dst_of(t0 + 3 * THREADS) = v3;
+    };
+    stage(threadIdx.x, true);
+    for (int t0 = threadIdx.x + 4 * THREADS; t0 < units; t0 += 4 * THREADS) stage(t0, false);
     __syncthreads();
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_next(rb[d]);
   }
-  load_next(r1);
-  load_next(r2);
 
   float acc[BATCH];
 #pragma unroll
@@ -417,16 +493,13 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
     }
   };
 
-  for (int t = 0; t < total; t += 3) {
-    consume(r0);
-    load_next(r0);
-    if (t + 1 < total) {
-      consume(r1);
-      load_next(r1);
-    }
-    if (t + 2 < total) {
-      consume(r2);
-      load_next(r2);
+  for (int t = 0; t < total; t += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (d == 0 || t + d < total) {
+        consume(rb[d]);
+        load_next(rb[d]);
+      }
     }
   }
 }

@@ -1,0 +1,338 @@
+// GEMV on the matrix cores ("Feasibility Report: Porting ROCmFP4 to Atlas", "Kernel
+// System": the decode gemv), for activation batches of 1..8 rows.
+//
+//   y[b][r] = sum_c weight(r, c) * x[b][c]
+//
+// Mapping. A workgroup of W wavefronts owns 16 consecutive weight rows (one MFMA tile
+// of v_mfma_f32_16x16x32_{f16,bf16}). Lane l of a wavefront serves as B-operand lane for
+// weight row l % 16 and as A-operand lane for activation row l % 16 (rows beyond the
+// batch read a clamped, finite row whose results are never stored); the lane group
+// l / 16 and the wavefront index pick which units of the row the lane streams: lane
+// group g = 4 w + l / 16 takes units g, g + 4W, g + 8W, ... (a unit is P = 1 or 2
+// consecutive blocks, loaded as in the dot-product kernel). The sum over k is order
+// free, so each MFMA adds, for every lane group, 8 consecutive weights of that lane's
+// own unit against the matching 8 activations: block j gives four MFMA steps s = 0..3
+// over weights 8s .. 8s+7 (low nibbles of qs words 0, 1 / 2, 3, then the high nibbles),
+// and the activation chunk of step s is the 16-byte unit s of the block.
+//
+// Decode. Each workgroup builds a 128-entry LDS table: for every value of a scale byte's
+// low seven bits, the f16 (or bf16) encodings of the eight magnitudes times the decoded
+// scale, as a plane of low bytes and a plane of high bytes. Every such product is exact
+// in both formats (at most 8 significant bits, between 2^-10 and 2400). Four weights
+// then take two v_perm_b32 gathers, an OR of the sign bits into the high bytes and two
+// interleaving v_perm_b32; the scale is part of the table, so the MFMA products are the
+// exact weight times activation products, summed in fp32.
+//
+// The W wavefronts' 16 x 16 accumulator tiles are added in LDS in a fixed order and
+// the batch rows are stored.
+
+#pragma once
+
+#include <type_traits>
+
+#include "gemv_impl.h"
+
+namespace rfp4 {
+namespace {
+
+typedef _Float16 mf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
+typedef float mf32x4 __attribute__((ext_vector_type(4)));
+
+template <int XT>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<kF16> {
+  static __device__ __forceinline__ mf32x4 mfma(uint4 a, uint4 b, mf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mf16x8, a),
+                                                  __builtin_bit_cast(mf16x8, b), c, 0, 0, 0);
+  }
+  // Encoding of an exactly representable value.
+  static __device__ __forceinline__ uint32_t enc(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+  }
+};
+
+template <>
+struct MfmaOps<kBF16> {
+  static __device__ __forceinline__ mf32x4 mfma(uint4 a, uint4 b, mf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8, a),
+                                                   __builtin_bit_cast(mbf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t enc(float v) { return __float_as_uint(v) >> 16; }
+};
+
+// Four weights of one nibble plane: `idx` holds their 3-bit magnitude indices in bytes
+// 0..3, `sgn` their sign bits at bit 7 of bytes 0..3, `t` the table entry of the scale
+// (low-byte plane of magnitudes 0-3, 4-7, then the high-byte plane). Returns the 16-bit
+// encodings of weights 0, 1 and 2, 3 as two words.
+__device__ __forceinline__ uint2 decode_plane(uint32_t idx, uint32_t sgn, uint4 t) {
+  const uint32_t lo = __builtin_amdgcn_perm(t.y, t.x, idx);
+  const uint32_t hi = __builtin_amdgcn_perm(t.w, t.z, idx) | sgn;
+  return uint2{__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)};
+}
+
+// The two scale bytes of block B of a unit (dual: e0, e1; fast: e, e).
+template <int LAYOUT, int P, int B>
+__device__ __forceinline__ void unit_scale_bytes(const UnitRaw<P>& u, uint32_t& e0, uint32_t& e1) {
+  constexpr int off = (P == 1) ? 16 : B * block_bytes(LAYOUT) + 16;
+  constexpr int wi = off / 4;
+  constexpr int bi = off % 4;
+  const uint32_t word = u.d[wi] >> (8 * bi);
+  e0 = word & 0x7Fu;
+  e1 = LAYOUT == kDual ? (word >> 8) & 0x7Fu : e0;
+}
+
+template <int LAYOUT, int XT, int P, bool XLDS, int W, int NP>
+__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvParts<NP> parts, int nu,
+                                                           const uint16_t* __restrict__ x,
+                                                           int64_t ldx, int batch) {
+  constexpr int UB = P * block_bytes(LAYOUT);
+  constexpr int THREADS = 64 * W;
+  typedef MfmaOps<XT> M;
+  extern __shared__ uint4 smem_m[];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;  // weight row of the tile (B) and activation row (A)
+  const int g = 4 * wv + (lane >> 4);  // lane group: units g, g + 4W, ...
+  const int xrows = XLDS ? batch * nu * (4 * P + 1) : 0;  // 16-byte LDS units of x
+  uint4* const xs = smem_m;
+  uint4* const lut = smem_m + xrows;
+  mf32x4* const red = reinterpret_cast<mf32x4*>(lut + 128);
+
+  // Part and row of this workgroup's tile.
+  const int tile = blockIdx.x;
+  int mi = 0;
+  if constexpr (NP > 1)
+    while (mi + 1 < parts.count && tile >= parts.gbeg[mi + 1]) ++mi;
+  const int n_part = NP > 1 ? parts.n[mi] : parts.n[0];
+  const int r0 = (tile - (NP > 1 ? parts.gbeg[mi] : 0)) * 16;
+  const int64_t rowbytes = static_cast<int64_t>(nu) * UB;
+  const uint8_t* const wrow =
+      (NP > 1 ? parts.w[mi] : parts.w[0]) + static_cast<int64_t>(min(r0 + col, n_part - 1)) * rowbytes;
+
+  // Units of this lane: u(t) = g + 4W t, t < T; past the row end the address is clamped
+  // and the weights are zeroed.
+  const int T = (nu + 4 * W - 1) / (4 * W);
+  auto unit_ptr = [&](int t) { return wrow + static_cast<int64_t>(min(g + 4 * W * t, nu - 1)) * UB; };
+
+  // Decode table (threads 0..127).
+  if (threadIdx.x < 128) {
+    const float sv = scale_exact(threadIdx.x);
+    const float mags[8] = {0.f, 1.f, 2.f, 3.f, 4.f, 6.f, 8.f, 10.f};
+    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t e = M::enc(mags[i] * sv);
+      lo[i >> 2] |= (e & 0xFFu) << (8 * (i & 3));
+      hi[i >> 2] |= (e >> 8) << (8 * (i & 3));
+    }
+    lut[threadIdx.x] = uint4{lo[0], lo[1], hi[0], hi[1]};
+  }
+
+  // Activations: the first loads are issued before the weight units so that the LDS
+  // stores wait only for them.
+  UnitRaw<P> rb[3];
+  if constexpr (XLDS) {
+    const int units = batch * 4 * nu * P;
+    auto src_of = [&](int t) {
+      const int cc = t & 3;
+      const int jb = t >> 2;
+      const int b = jb / (nu * P);
+      const int j = jb - b * nu * P;
+      return reinterpret_cast<const uint4*>(x + b * ldx + 32 * j + 8 * cc);
+    };
+    auto dst_of = [&](int t) {
+      const int cc = t & 3;
+      const int jb = t >> 2;
+      const int b = jb / (nu * P);
+      const int j = jb - b * nu * P;
+      return xs + xs_index<P>(b, j / P, nu, j % P, cc);
+    };
+    const int t0 = threadIdx.x;
+    const uint4 v0 = *src_of(min(t0, units - 1));
+    const uint4 v1 = *src_of(min(t0 + THREADS, units - 1));
+#pragma unroll
+    for (int d = 0; d < 3; ++d) load_unit<LAYOUT, P>(unit_ptr(d), rb[d]);
+    if (t0 < units) *dst_of(t0) = v0;
+    if (t0 + THREADS < units) *dst_of(t0 + THREADS) = v1;
+    for (int t = t0 + 2 * THREADS; t < units; t += THREADS) *dst_of(t) = *src_of(t);
+  } else {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) load_unit<LAYOUT, P>(unit_ptr(d), rb[d]);
+  }
+  __syncthreads();
+
+  const int xb = min(col, batch - 1);  // activation row of this A lane (clamped)
+  mf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  auto consume = [&](const UnitRaw<P>& u, int t) {
+    const int uidx = g + 4 * W * t;
+    const bool valid = uidx < nu;
+    const int uc = min(uidx, nu - 1);
+    auto block = [&](auto b_c) {
+      constexpr int B = decltype(b_c)::value;
+      uint4 q = unit_qs<LAYOUT, P, B>(u);
+      if (!valid) q = uint4{0u, 0u, 0u, 0u};
+      uint32_t e0, e1;
+      unit_scale_bytes<LAYOUT, P, B>(u, e0, e1);
+      const uint4 t0 = lut[e0];
+      const uint4 t1 = LAYOUT == kDual ? lut[e1] : t0;
+      auto xop = [&](int s) -> uint4 {
+        if constexpr (XLDS)
+          return xs[xs_index<P>(xb, uc, nu, B, s)];
+        else
+          return *reinterpret_cast<const uint4*>(x + xb * ldx + 32 * (P * uc + B) + 8 * s);
+      };
+      const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t qa = qw[2 * (s & 1)], qb = qw[2 * (s & 1) + 1];
+        uint2 pa, pb;
+        if (s < 2) {  // low nibbles: first half (scale e0)
+          pa = decode_plane(qa & 0x07070707u, (qa << 4) & 0x80808080u, t0);
+          pb = decode_plane(qb & 0x07070707u, (qb << 4) & 0x80808080u, t0);
+        } else {  // high nibbles: second half (scale e1)
+          pa = decode_plane((qa >> 4) & 0x07070707u, qa & 0x80808080u, t1);
+          pb = decode_plane((qb >> 4) & 0x07070707u, qb & 0x80808080u, t1);
+        }
+        acc = M::mfma(xop(s), uint4{pa.x, pa.y, pb.x, pb.y}, acc);
+      }
+    };
+    block(std::integral_constant<int, 0>{});
+    if constexpr (P == 2) block(std::integral_constant<int, 1>{});
+  };
+
+  for (int t = 0; t < T; t += 3) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      if (d == 0 || t + d < T) {
+        consume(rb[d], t + d);
+        if (t + d + 3 < T) load_unit<LAYOUT, P>(unit_ptr(t + d + 3), rb[d]);
+      }
+    }
+  }
+
+  // Lane l, register i holds batch row 4 (l / 16) + i of weight row l % 16.
+  float* const y = NP > 1 ? parts.y[mi] : parts.y[0];
+  const int64_t ldy = NP > 1 ? parts.ldy[mi] : parts.ldy[0];
+  if constexpr (W > 1) {
+    red[wv * 64 + lane] = acc;
+    __syncthreads();
+    if (wv != 0) return;
+    for (int w = 1; w < W; ++w) {
+      const mf32x4 o = red[w * 64 + lane];
+      acc[0] += o[0];
+      acc[1] += o[1];
+      acc[2] += o[2];
+      acc[3] += o[3];
+    }
+  }
+  const int row = r0 + col;
+  if (row < n_part) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * (lane >> 4) + i;
+      if (b < batch) y[b * ldy + row] = acc[i];
+    }
+  }
+}
+
+struct MfmaPlan {
+  int p, nu, w, tiles;
+  bool xlds;
+  size_t shm;
+};
+
+// Wavefronts per workgroup: the most (up to 16) that keep the launch within about 24
+// wavefronts per CU and give every lane group at least one unit.
+inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch) {
+  MfmaPlan pl;
+  pl.p = nb % 2 == 0 ? 2 : 1;
+  pl.nu = nb / pl.p;
+  pl.tiles = 0;
+  for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 15) / 16);
+  const int64_t target = 24LL * device_cu_count();
+  pl.w = 4;
+  for (int w = 16; w >= 8; w /= 2) {
+    if (static_cast<int64_t>(pl.tiles) * w <= target && 4 * w <= pl.nu) {
+      pl.w = w;
+      break;
+    }
+  }
+  const size_t xbytes = static_cast<size_t>(batch) * pl.nu * (4 * pl.p + 1) * 16;
+  const size_t fixed = 128 * 16 + static_cast<size_t>(pl.w) * 64 * 16;
+  pl.xlds = xbytes + fixed <= 64 * 1024;
+  pl.shm = (pl.xlds ? xbytes : 0) + fixed;
+  return pl;
+}
+
+template <int LAYOUT, int XT, int P, bool XLDS, int NP>
+hipError_t launch_mfma_w(const MfmaPlan& pl, const GemvParts<NP>& gp, const uint16_t* x, int64_t ldx,
+                         int batch, hipStream_t stream) {
+  const dim3 grid(pl.tiles), block(64 * pl.w);
+  switch (pl.w) {
+    case 16:
+      gemv_mfma_kernel<LAYOUT, XT, P, XLDS, 16, NP><<<grid, block, pl.shm, stream>>>(gp, pl.nu, x, ldx, batch);
+      break;
+    case 8:
+      gemv_mfma_kernel<LAYOUT, XT, P, XLDS, 8, NP><<<grid, block, pl.shm, stream>>>(gp, pl.nu, x, ldx, batch);
+      break;
+    default:
+      gemv_mfma_kernel<LAYOUT, XT, P, XLDS, 4, NP><<<grid, block, pl.shm, stream>>>(gp, pl.nu, x, ldx, batch);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int LAYOUT, int XT, int NP>
+hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t* x, int batch,
+                       int64_t ldx, hipStream_t stream) {
+  const MfmaPlan pl = mfma_plan(parts, count, nb, batch);
+  GemvParts<NP> gp;
+  gp.count = count;
+  gp.gbeg[0] = 0;
+  for (int i = 0; i < count; ++i) {
+    gp.w[i] = parts[i].w;
+    gp.y[i] = parts[i].y;
+    gp.ldy[i] = parts[i].ldy;
+    gp.n[i] = static_cast<int>(parts[i].n);
+    gp.gbeg[i + 1] = gp.gbeg[i] + static_cast<int>((parts[i].n + 15) / 16);
+  }
+  if (pl.p == 2)
+    return pl.xlds ? launch_mfma_w<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, stream)
+                   : launch_mfma_w<LAYOUT, XT, 2, false, NP>(pl, gp, x, ldx, batch, stream);
+  return pl.xlds ? launch_mfma_w<LAYOUT, XT, 1, true, NP>(pl, gp, x, ldx, batch, stream)
+                 : launch_mfma_w<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, stream);
+}
+
+// Matrix-core path for the batches where it is faster: measured on the decode shapes,
+// the dot-product kernel wins at batch 1 (its decode needs no table and no cross-wave
+// reduction), the two tie at batch 2, and the matrix cores win from batch 4 on (the
+// dot-product work grows with the batch, the decode here does not; 3.7x at batch 8).
+// The environment variable RFP4_GEMV_MFMA = "0" selects the dot-product kernel and "1"
+// the matrix cores for every batch; otherwise batches >= RFP4_GEMV_MFMA_MIN_BATCH.
+#ifndef RFP4_GEMV_MFMA_MIN_BATCH
+#define RFP4_GEMV_MFMA_MIN_BATCH 3
+#endif
+inline bool use_mfma(int batch) {
+  const char* env = getenv("RFP4_GEMV_MFMA");
+  if (env != nullptr && env[0] == '0') return false;
+  if (env != nullptr && env[0] == '1') return true;
+  return batch >= RFP4_GEMV_MFMA_MIN_BATCH;
+}
+
+template <int XT>
+hipError_t launch_gemv_mfma_xt(const GemvPart* parts, int count, int layout, int nb, const uint16_t* x,
+                               int batch, int64_t ldx, hipStream_t s) {
+  if (count == 1)
+    return layout == kDual ? launch_mfma<kDual, XT, 1>(parts, count, nb, x, batch, ldx, s)
+                           : launch_mfma<kFast, XT, 1>(parts, count, nb, x, batch, ldx, s);
+  return layout == kDual ? launch_mfma<kDual, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, s)
+                         : launch_mfma<kFast, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, s);
+}
+
+}  // namespace
+}  // namespace rfp4

@@ -224,6 +224,7 @@ GEMV_PLANS = [
 @pytest.mark.parametrize("case", GEMV_PLANS, ids=lambda c: "{}-L{}n{}k{}b{}{}".format(*c))
 def test_gemv_forced_plan(case, monkeypatch):
     plan, layout, n, k, batch, dt = case
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")  # lane mappings of the dot-product kernel
     monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
     rng = np.random.default_rng(5000 + n + k + batch)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
@@ -257,6 +258,7 @@ def test_gemv_multi(case):
 def test_gemv_multi_equals_single_calls(monkeypatch):
     """With the same (forced) lane mapping the fused launch gives exactly the results of
     separate calls."""
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")
     monkeypatch.setenv("RFP4_GEMV_PLAN", "2:16")
     rng = np.random.default_rng(77)
     ns, k = [640, 96, 96], 2048
@@ -629,6 +631,7 @@ def test_unaligned_rows_gemv(case):
 def test_unaligned_rows_gemv_forced_plan(case, plan, monkeypatch):
     """Every lane mapping on rows at all byte offsets (an odd block count ignores a
     forced P = 2 and takes single-block units)."""
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")
     monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
     layout, n, k, batch, dt = case
     rng = np.random.default_rng(8200 + n + k)
@@ -711,3 +714,71 @@ def test_unaligned_rows_gemm_dequant(case):
     torch.cuda.synchronize()
     c_ref, den = O.gemm(w, layout, n, k, x64(a))
     assert gemm_error(c.to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
+
+
+# ------------------------------------------------------------------ GEMV on the matrix cores
+# Both GEMV kernels are checked at every batch by forcing the path: RFP4_GEMV_MFMA=1 runs
+# the matrix-core kernel (16-row tiles, table decode, k split over the wavefronts of a
+# workgroup), =0 the dot-product kernel. Cases cover ragged row counts, odd block counts
+# (single-block units), rows that are not 16-byte multiples, activations staged in LDS and
+# read from global memory (long rows, large batches), every wavefront count, and fused
+# launches.
+
+MFMA_CASES = [  # layout, n, k, batch, dtype
+    (0, 17408, 5120, 1, "f16"), (0, 17408, 5120, 8, "f16"), (1, 5120, 17408, 1, "bf16"),
+    (1, 5120, 17408, 8, "bf16"), (0, 6144, 5120, 3, "bf16"), (0, 1024, 5120, 5, "f16"),
+    (0, 1, 256, 1, "f16"), (1, 7, 512, 2, "bf16"), (0, 33, 1408, 4, "f16"), (1, 45, 1056, 6, "bf16"),
+    (0, 130, 96, 7, "f16"), (1, 17, 32, 8, "bf16"), (0, 300, 4000, 8, "bf16"), (1, 64, 99968, 2, "f16"),
+    (0, 999, 2304, 8, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=lambda c: "L{}n{}k{}b{}{}".format(*c))
+def test_gemv_mfma(case, monkeypatch):
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    layout, n, k, batch, dt = case
+    rng = np.random.default_rng(9000 + n + k + batch)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    x = synth.activations(rng, batch, k, dt)
+    check_gemv(w, layout, n, k, x, ldy=n + 3)
+
+
+@pytest.mark.parametrize("batch", [2, 8])
+def test_gemv_dot_product_kernel_large_batch(batch, monkeypatch):
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")
+    w, x, cfg = synth.gemv_inputs("down", batch=batch)
+    check_gemv(w, cfg["layout"], cfg["n"], cfg["k"], x)
+
+
+def test_gemv_mfma_padded_activations(monkeypatch):
+    """ldx > k and ldy > n on the matrix-core path."""
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    layout, n, k, batch = 0, 77, 768, 5
+    rng = np.random.default_rng(9100)
+    w = synth.weights(rng, layout, n, k)
+    x = synth.activations(rng, batch, k, "f16")
+    check_gemv(w, layout, n, k, x, ldx=k + 16, ldy=n + 9)
+
+
+@pytest.mark.parametrize("case", MULTI, ids=lambda c: "L{}p{}k{}b{}{}".format(c[0], len(c[1]), *c[2:]))
+def test_gemv_mfma_multi(case, monkeypatch):
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    layout, ns, k, batch, dt = case
+    rng = np.random.default_rng(9200 + sum(ns) + k + batch)
+    ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
+    x = synth.activations(rng, batch, k, dt)
+    ys = R.rfp4_gemv_multi([dev(w) for w in ws], layout, ns, k, x.to(DEV).contiguous())
+    torch.cuda.synchronize()
+    for w, n, y in zip(ws, ns, ys):
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
+
+
+def test_gemv_mfma_zero_scales_give_zero(monkeypatch):
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    layout, n, k, batch = 0, 40, 512, 4
+    w = synth.weights(np.random.default_rng(9300), layout, n, k).reshape(n, k // 32, 18)
+    w[:, :, 16:] = 0
+    x = synth.activations(np.random.default_rng(9301), batch, k, "bf16")
+    y = run_gemv(w.reshape(n, -1), layout, n, k, x)
+    assert np.all(y == 0.0)
