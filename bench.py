@@ -36,8 +36,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATE_MIN_BYTES = 600 * 2**20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_up.json")
-GEMV_SOURCES = ["gemm_rfp4_block_amd/csrc/gemv_impl.h", "gemm_rfp4_block_amd/csrc/gemv_f16.hip",
-                "gemm_rfp4_block_amd/csrc/gemv.hip", "gemm_rfp4_block_amd/csrc/rfp4_decode.h"]
+GEMV_SOURCES = ["gemm_rfp4_block_amd/csrc/gemv_impl.h", "gemm_rfp4_block_amd/csrc/gemv_mfma.h",
+                "gemm_rfp4_block_amd/csrc/gemv_f16.hip", "gemm_rfp4_block_amd/csrc/gemv.hip",
+                "gemm_rfp4_block_amd/csrc/rfp4_decode.h"]
 
 
 def log(*a):
