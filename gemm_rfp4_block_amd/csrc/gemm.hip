@@ -36,6 +36,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <type_traits>
@@ -807,21 +809,39 @@ hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint
   return hipGetLastError();
 }
 
-// Relative times used to choose a plan: one round of 128 x 128 tail tiles (full k) and
-// the reduction of split partial sums, each against one round of main tiles.
-constexpr double kTailRoundCost = 0.35;
-constexpr double kReduceCost = 0.03;
+// Cost model of a plan, fitted to measured launches on MI355X (2048 x 17408 x 5120,
+// 4096 x 17408 x 5120, 2048 x 5120 x 17408, 2048 x 5120 x 6144, 2048 x 6144 x 5120,
+// 2048 x 1024 x 5120, 512 x 17408 x 5120 under every plan): a round of workgroups (one
+// per CU) costs kMainUsPerK (256 x 256 tiles) or kTailUsPerK (128 x 128 tiles) times its
+// k columns; a last, partial round filling a fraction f of the CUs costs f^kPartialExp
+// of a full one (fewer busy CUs run faster); a split adds a reduction that moves its
+// partial sums at kReduceBytesPerUs plus kReduceFixedUs. It ranks the measured plans of
+// those shapes in the measured order of their best.
+constexpr double kMainUsPerK = 0.030;
+constexpr double kTailUsPerK = 0.012;
+constexpr double kPartialExp = 0.4;
+constexpr double kReduceBytesPerUs = 3.8e6;
+constexpr double kReduceFixedUs = 5.0;
 
 struct Plan {
   int64_t tail_strips;  // trailing 256-column strips of C computed with tail tiles
   int splits;           // k-range split of each tail tile
   int64_t tail_tiles;   // tail tiles (before the split)
+  int main_splits = 1;  // k-range split of each main tile
+  int64_t main_tiles = 0;
 };
 
-// Chooses the tail strips and split that minimize rounds of main tiles plus weighted
-// rounds of tail tiles (per split) plus the reduction. RFP4_GEMM_PLAN = "main", "tail",
-// "tail2" or "tail4" forces all-main tiles or all-tail tiles with that split (lets tests
-// cover every path at small sizes); "nosplit" keeps the choice of strips but no split.
+inline double rounds(int64_t workgroups, int cus) {
+  const int64_t full = workgroups / cus;
+  const double frac = static_cast<double>(workgroups % cus) / cus;
+  return static_cast<double>(full) + (frac > 0.0 ? std::pow(frac, kPartialExp) : 0.0);
+}
+
+// Chooses the tail strips and the splits of main and tail tiles with the lowest modelled
+// time. RFP4_GEMM_PLAN = "main", "tail", "tail2", "tail4", "msplit2", "msplit3" or
+// "msplit4" forces all-main tiles, all-tail tiles with that split, or all-main tiles
+// with that split (lets tests cover every path at small sizes); "nosplit" chooses among
+// the plans without a split.
 Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
   const int64_t strips = (n + MainCfg::BN - 1) / MainCfg::BN;
   const int64_t mt = (m + MainCfg::BM - 1) / MainCfg::BM;
@@ -831,29 +851,43 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
     return t > 0 ? slabs * ((cols + TailCfg::BN - 1) / TailCfg::BN) : 0;
   };
   const int max_split = (nb + 3) / 4;  // each split needs at least two 64-column steps
+  const double k = 32.0 * nb;
   const char* env = getenv("RFP4_GEMM_PLAN");
   const std::string plan = env != nullptr ? env : "";
-  if (plan == "main") return Plan{0, 1, 0};
+  if (plan == "main") return Plan{0, 1, 0, 1, mt * strips};
+  if (plan == "msplit2" || plan == "msplit3" || plan == "msplit4")
+    return Plan{0, 1, 0, std::min(plan[6] - '0', max_split), mt * strips};
   if (plan == "tail" || plan == "tail2" || plan == "tail4") {
     int sp = plan == "tail" ? 1 : (plan == "tail2" ? 2 : 4);
     if (sp > max_split) sp = max_split;
     return Plan{strips, sp, tail_tiles(strips)};
   }
   const bool allow_split = plan != "nosplit";
-  Plan best{0, 1, 0};
+  auto reduce_us = [](int64_t tiles, int sp, int tile_elems) {
+    return sp > 1 ? (static_cast<double>(tiles) * tile_elems * (4.0 * sp + 2.0)) / kReduceBytesPerUs +
+                        kReduceFixedUs
+                  : 0.0;
+  };
+  Plan best{0, 1, 0, 1, mt * strips};
   double best_cost = 1e300;
   const int64_t max_tail = strips < 256 ? strips : 256;
   for (int64_t t = 0; t <= max_tail; ++t) {
     const int64_t main_tiles = mt * (strips - t);
     const int64_t tt = tail_tiles(t);
-    for (int sp = 1; sp <= 8; sp *= 2) {
-      if (sp > 1 && (!allow_split || sp > max_split || tt == 0)) break;
-      const double rounds_main = static_cast<double>((main_tiles + cus - 1) / cus);
-      const double rounds_tail = static_cast<double>((tt * sp + cus - 1) / cus);
-      const double cost = rounds_main + kTailRoundCost * rounds_tail / sp + (sp > 1 ? kReduceCost : 0.0);
-      if (cost < best_cost - 1e-9) {
-        best_cost = cost;
-        best = Plan{t, sp, tt};
+    for (int spm = 1; spm <= 4; ++spm) {
+      if (spm > 1 && (!allow_split || spm > max_split || main_tiles == 0)) break;
+      const double cm = main_tiles > 0 ? kMainUsPerK * k / spm * rounds(main_tiles * spm, cus) +
+                                             reduce_us(main_tiles, spm, MainCfg::BM * MainCfg::BN)
+                                       : 0.0;
+      for (int sp = 1; sp <= 8; sp *= 2) {
+        if (sp > 1 && (!allow_split || sp > max_split || tt == 0)) break;
+        const double ct = tt > 0 ? kTailUsPerK * k / sp * rounds(tt * sp, cus) +
+                                       reduce_us(tt, sp, TailCfg::BM * TailCfg::BN)
+                                 : 0.0;
+        if (cm + ct < best_cost - 1e-9) {
+          best_cost = cm + ct;
+          best = Plan{t, sp, tt, spm, main_tiles};
+        }
       }
     }
   }
@@ -925,21 +959,30 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
   for (int64_t m_off = 0; m_off < m; m_off += max_m) {
     const int mc = static_cast<int>(m - m_off < max_m ? m - m_off : max_m);
     Plan plan = choose_plan(mc, n, nb, cus);
-    float* partial = nullptr;
-    if (plan.splits > 1) {
-      const size_t bytes = static_cast<size_t>(plan.tail_tiles) * plan.splits * TailCfg::BM *
-                           TailCfg::BN * sizeof(float);
-      if (split_workspace(stream, bytes, &partial) != hipSuccess) {
-        (void)hipGetLastError();  // clear a failed allocation; run the tail unsplit
+    float* partial = nullptr;       // tail partial sums
+    float* partial_main = nullptr;  // main partial sums (before the tail's)
+    const size_t main_bytes = plan.main_splits > 1 ? static_cast<size_t>(plan.main_tiles) * plan.main_splits *
+                                                         MainCfg::BM * MainCfg::BN * sizeof(float)
+                                                   : 0;
+    const size_t tail_bytes = plan.splits > 1 ? static_cast<size_t>(plan.tail_tiles) * plan.splits *
+                                                    TailCfg::BM * TailCfg::BN * sizeof(float)
+                                              : 0;
+    if (main_bytes + tail_bytes > 0) {
+      float* ws = nullptr;
+      if (split_workspace(stream, main_bytes + tail_bytes, &ws) != hipSuccess) {
+        (void)hipGetLastError();  // clear a failed allocation; run every tile unsplit
         plan.splits = 1;
-        partial = nullptr;
+        plan.main_splits = 1;
+      } else {
+        partial_main = ws;
+        partial = ws + main_bytes / sizeof(float);
       }
     }
     const int64_t n_split = (strips - plan.tail_strips) * MainCfg::BN;
     const uint16_t* ap = a + m_off * lda;
     uint16_t* cp = c + m_off * ldc;
     e = launch_region<MainCfg>(w, layout, static_cast<int>(n), nb, ap, mc, lda, cp, ldc, 0, n_split,
-                               1, nullptr, stream);
+                               plan.main_splits, partial_main, stream);
     if (e != hipSuccess) return e;
     e = launch_region<TailCfg>(w, layout, static_cast<int>(n), nb, ap, mc, lda, cp, ldc, n_split, n,
                                plan.splits, partial, stream);

@@ -143,16 +143,18 @@ RFP4_API rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int6
  * fp32 accumulation. lda >= k (lda % 8 == 0), ldc >= n (ldc % 8 == 0), and
  * m * lda, m * ldc <= 2^39 (RFP4_ERR_SHAPE otherwise).
  * Balance: the columns of C are split between 256 x 256 tiles and trailing strips of
- * 128 x 128 tiles whose k range may be split in two or more parts, so that the CUs
- * get equal work. Split tiles write fp32 partial sums to a device workspace that the
+ * 128 x 128 tiles, and the k range of either kind of tile may be split in two or more
+ * parts, as a cost model of the launch picks. Split tiles write fp32 partial sums to a
+ * device workspace that the
  * library allocates per (device, stream) on first need, grows when a larger one is
  * needed (synchronizing that stream first) and keeps until the process ends; a
  * final kernel adds the parts in a fixed order and rounds to bf16. The workspace is
  * never allocated while the stream is being captured into a graph (the split is
  * then skipped), so call once before capturing. Results are deterministic for a
  * given shape and CU count. The environment variable RFP4_GEMM_PLAN, read on each
- * call, forces a plan: "main" (256 x 256 tiles only), "tail", "tail2", "tail4"
- * (128 x 128 tiles only, k unsplit or split 2 or 4 ways), "nosplit". */
+ * call, forces a plan: "main" (256 x 256 tiles only), "msplit2", "msplit3", "msplit4"
+ * (256 x 256 tiles only, k split 2, 3 or 4 ways), "tail", "tail2", "tail4" (128 x 128
+ * tiles only, k unsplit or split 2 or 4 ways), "nosplit" (no k split). */
 RFP4_API rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
                       int64_t m, int64_t lda, void* c, int64_t ldc, void* stream);
 

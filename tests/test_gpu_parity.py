@@ -418,7 +418,7 @@ def test_gemm_same_sign_rounding():
     assert np.all(np.abs(c - ref_bf) <= ulp + 1e-30)
 
 
-@pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4"])
+@pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4", "msplit2", "msplit3", "msplit4"])
 @pytest.mark.parametrize("case", [(0, 100, 200, 512), (1, 77, 136, 1024), (0, 257, 520, 2304),
                                   (1, 300, 264, 512)], ids=lambda c: "L{}m{}n{}k{}".format(*c))
 def test_gemm_forced_tile_size(case, plan, monkeypatch):
@@ -431,6 +431,18 @@ def test_gemm_forced_tile_size(case, plan, monkeypatch):
     c = run_gemm(w, layout, n, k, a, ldc=n + 8)
     c_ref, den = O.gemm(w, layout, n, k, x64(a))
     assert gemm_error(c, c_ref, den) <= TOL
+
+
+def test_gemm_split_main_tiles_full_size_sampled(monkeypatch):
+    """The 2048 x 5120 x 17408 down-projection prefill, for which the planner splits the
+    k range of the 256 x 256 tiles three ways; checked on sampled columns."""
+    layout, m, n, k = 1, 2048, 5120, 17408
+    w = synth.weights(np.random.default_rng(4400), layout, n, k, stress_frac=0.01)
+    a = synth.activations(np.random.default_rng(4401), m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a)
+    cols = np.unique(np.concatenate([np.random.default_rng(4402).choice(n, 40, replace=False), [0, 255, 256, n - 1]]))
+    c_ref, den = O.gemm_rows(w, layout, n, k, x64(a), cols)
+    assert gemm_error(c[:, cols], c_ref, den) <= TOL
 
 
 def test_gemm_mixed_tile_sizes():
@@ -669,7 +681,7 @@ def test_unaligned_rows_gemm(case):
     assert gemm_error(c, c_ref, den) <= TOL
 
 
-@pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4"])
+@pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4", "msplit3"])
 @pytest.mark.parametrize("case", [(0, 100, 200, 96), (1, 130, 264, 544), (0, 257, 300, 1376)],
                          ids=lambda c: "L{}m{}n{}k{}".format(*c))
 def test_unaligned_rows_gemm_forced_tile_size(case, plan, monkeypatch):
