@@ -604,20 +604,27 @@ template <int LAYOUT, int XT, int BATCH, int NP>
 hipError_t launch3(const GemvPart* parts, int count, int nb, const uint16_t* x, int64_t ldx,
                    hipStream_t stream) {
   // Activation bytes in LDS (largest unit size: 4P+1 units of 16 bytes per P blocks).
+  // Long rows are staged in the layout of the units the plan uses: pairs of blocks (9
+  // chunks per 2 blocks) when the block count is even, else single blocks (5 per block).
   const size_t xbytes1 = static_cast<size_t>(BATCH) * nb * 5 * 16;
   const size_t xbytes2 = static_cast<size_t>(BATCH) * (nb / 2) * 9 * 16;
+  const size_t xbytes_large = nb % 2 == 0 ? xbytes2 : xbytes1;
   const bool small_x = xbytes1 <= static_cast<size_t>(kXLdsBudget);
-  const bool large_x = !small_x && xbytes1 <= static_cast<size_t>(kXLdsBudgetLarge);
+  const bool large_x = !small_x && xbytes_large <= static_cast<size_t>(kXLdsBudgetLarge);
   const bool xlds = small_x || large_x;
   const int threads = large_x ? kThreadsLarge : kThreadsSmall;
+  const size_t xbytes_fit = large_x ? xbytes_large : xbytes1;
   // Resident wavefronts per CU: the knob (two whole 16-wavefront workgroups for long
   // rows), capped by what LDS allows (160 KB per CU).
   int waves_per_cu = large_x ? 2 * (kThreadsLarge / 64) : RFP4_GEMV_WAVES_PER_CU;
   if (xlds) {
-    const int wg_fit = static_cast<int>((160 * 1024) / xbytes1);
+    const int wg_fit = static_cast<int>((160 * 1024) / xbytes_fit);
     if (wg_fit * (threads / 64) < waves_per_cu) waves_per_cu = wg_fit * (threads / 64);
   }
   Plan pl = choose_plan(parts, count, nb, waves_per_cu, xlds, threads);
+  // A forced single-block mapping whose staging layout would not fit takes pairs.
+  if (large_x && pl.p == 1 && xbytes1 > static_cast<size_t>(kXLdsBudgetLarge))
+    pl = make_plan(2, pl.log2cl, parts, count, nb, waves_per_cu, threads);
   // Activations from global memory: single blocks per unit (a forced P = 2 mapping keeps
   // its lane count).
   if (!xlds && pl.p == 2) pl = make_plan(1, pl.log2cl, parts, count, nb, waves_per_cu, threads);
