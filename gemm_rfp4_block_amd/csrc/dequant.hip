@@ -12,6 +12,13 @@
 #include "rfp4_decode.h"
 #include "rfp4_internal.h"
 
+// Output stores are non-temporal (the output is written once and not read back by this
+// kernel): measured on the up-projection matrix, fp32 out 83.6 -> 56.9 us (4.9 -> 7.2 TB/s),
+// bf16 out 34.5 -> 33.4 us. RFP4_DEQUANT_NT=0 builds ordinary stores.
+#ifndef RFP4_DEQUANT_NT
+#define RFP4_DEQUANT_NT 1
+#endif
+
 namespace rfp4 {
 namespace {
 
@@ -41,7 +48,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       v.y = a.y * sc;
       v.z = b.x * sc;
       v.w = b.y * sc;
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + row * ldo + j * 32 + 4 * s) = v;
+      float4* const dst = reinterpret_cast<float4*>(static_cast<float*>(out) + row * ldo + j * 32 + 4 * s);
+#if RFP4_DEQUANT_NT
+      typedef float nt4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(nt4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt4*>(dst));
+#else
+      *dst = v;
+#endif
     } else {
       // Thread s writes weights 8s .. 8s+7: the low (s < 2) or high (s >= 2) nibbles of
       // qs bytes 8(s % 2) .. 8(s % 2) + 7. Every value is a bf16 value, so keeping the
@@ -58,8 +71,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         o[i] = (__float_as_uint(v[i].x * sc) >> 16) | (__float_as_uint(v[i].y * sc) & 0xFFFF0000u);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + row * ldo + j * 32 + 8 * s) =
-          uint4{o[0], o[1], o[2], o[3]};
+      uint4* const dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + row * ldo + j * 32 + 8 * s);
+#if RFP4_DEQUANT_NT
+      typedef uint32_t ntu4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(ntu4{o[0], o[1], o[2], o[3]}, reinterpret_cast<ntu4*>(dst));
+#else
+      *dst = uint4{o[0], o[1], o[2], o[3]};
+#endif
     }
   }
 }

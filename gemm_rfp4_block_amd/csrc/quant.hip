@@ -231,8 +231,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const uint8_t* __r
     const int64_t nblk = min(static_cast<int64_t>(kSeg), total_blocks - first);
     const int bytes = static_cast<int>(nblk) * BB;
     uint8_t* o = out + first * BB;  // 16-byte aligned: kSeg * BB is a multiple of 16
-    for (int c = tid; c < bytes / 16; c += kQuantThreads)
-      *reinterpret_cast<uint4*>(o + 16 * c) = *reinterpret_cast<const uint4*>(seg_buf + 16 * c);
+    typedef uint32_t ntu4 __attribute__((ext_vector_type(4)));
+    for (int c = tid; c < bytes / 16; c += kQuantThreads)  // written once: non-temporal
+      __builtin_nontemporal_store(*reinterpret_cast<const ntu4*>(seg_buf + 16 * c),
+                                  reinterpret_cast<ntu4*>(o + 16 * c));
     const int tail = bytes & 15;
     if (tid < tail) o[bytes - tail + tid] = seg_buf[bytes - tail + tid];
     __syncthreads();
