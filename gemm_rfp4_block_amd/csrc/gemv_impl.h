@@ -105,6 +105,29 @@ __device__ __forceinline__ f16x2 spread_f16(uint32_t h, bool hi_pair) {
   return __builtin_bit_cast(f16x2, v);
 }
 
+// Weight loads (each weight byte is read once per launch). RFP4_GEMV_NT_LOADS selects
+// non-temporal loads (tuning knob, no effect on results); measured slower (up-projection
+// 12.5 -> 16.6 us): the loads of a unit share cache lines, which then are not kept.
+#ifndef RFP4_GEMV_NT_LOADS
+#define RFP4_GEMV_NT_LOADS 0
+#endif
+typedef uint32_t wu4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 wload16(const void* p) {
+#if RFP4_GEMV_NT_LOADS
+  const wu4 v = __builtin_nontemporal_load(static_cast<const wu4*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
+#else
+  return *static_cast<const uint4*>(p);
+#endif
+}
+__device__ __forceinline__ uint32_t wload4(const void* p) {
+#if RFP4_GEMV_NT_LOADS
+  return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+#else
+  return *static_cast<const uint32_t*>(p);
+#endif
+}
+
 // Raw bytes of one unit of P consecutive blocks (see the file comment), as words.
 //   P = 1: d[0..3] = index bytes, d[4] = the scale byte(s) in its low bytes.
 //   P = 2: d[0..7] = bytes 0..31, d[8] = bytes 32..35 (dual) or 32..33 (fast).
@@ -127,19 +150,19 @@ __device__ __forceinline__ void load_unit_realigned(const uint8_t* p, UnitRaw<P>
   const int sh = static_cast<int>(reinterpret_cast<uintptr_t>(p) & 3u);
   const uint32_t* a = reinterpret_cast<const uint32_t*>(p - sh);
   uint32_t wv[NW];
-  const uint4 v0 = *reinterpret_cast<const uint4*>(a);
+  const uint4 v0 = wload16(a);
   wv[0] = v0.x;
   wv[1] = v0.y;
   wv[2] = v0.z;
   wv[3] = v0.w;
   if constexpr (P == 2) {
-    const uint4 v1 = *reinterpret_cast<const uint4*>(a + 4);
+    const uint4 v1 = wload16(a + 4);
     wv[4] = v1.x;
     wv[5] = v1.y;
     wv[6] = v1.z;
     wv[7] = v1.w;
   }
-  wv[NW - 1] = a[NW - 1];
+  wv[NW - 1] = wload4(a + NW - 1);
 #pragma unroll
   for (int i = 0; i < NW - 1; ++i) u.d[i] = __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], sh);
   u.d[NW - 1] = wv[NW - 1] >> (8 * sh);
@@ -151,7 +174,7 @@ __device__ __forceinline__ void load_unit(const uint8_t* p, UnitRaw<P>& u) {
     load_unit_realigned<LAYOUT, P>(p, u);
     return;
   }
-  const uint4 v0 = load16(p);
+  const uint4 v0 = wload16(p);
   u.d[0] = v0.x;
   u.d[1] = v0.y;
   u.d[2] = v0.z;
@@ -165,13 +188,13 @@ __device__ __forceinline__ void load_unit(const uint8_t* p, UnitRaw<P>& u) {
       u.d[4] = p[16];
     }
   } else {
-    const uint4 v1 = load16(p + 16);
+    const uint4 v1 = wload16(p + 16);
     u.d[4] = v1.x;
     u.d[5] = v1.y;
     u.d[6] = v1.z;
     u.d[7] = v1.w;
     if constexpr (LAYOUT == kDual) {
-      u.d[8] = load4(p + 32);  // 4-byte aligned: units start at multiples of 36 bytes
+      u.d[8] = wload4(p + 32);  // 4-byte aligned: units start at multiples of 36 bytes
                                // (P = 2 needs an even block count, so rows hold 36j bytes)
     } else {
       uint16_t t;
