@@ -868,6 +868,11 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
                         kReduceFixedUs
                   : 0.0;
   };
+  // Partial sums of one launch stay within kMaxPartialBytes (the workspace is kept).
+  constexpr double kMaxPartialBytes = 512.0 * 1024 * 1024;
+  auto partial_ok = [&](int64_t tiles, int sp, int tile_elems) {
+    return sp == 1 || static_cast<double>(tiles) * sp * tile_elems * 4.0 <= kMaxPartialBytes;
+  };
   Plan best{0, 1, 0, 1, mt * strips};
   double best_cost = 1e300;
   const int64_t max_tail = strips < 256 ? strips : 256;
@@ -876,11 +881,13 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
     const int64_t tt = tail_tiles(t);
     for (int spm = 1; spm <= 4; ++spm) {
       if (spm > 1 && (!allow_split || spm > max_split || main_tiles == 0)) break;
+      if (!partial_ok(main_tiles, spm, MainCfg::BM * MainCfg::BN)) break;
       const double cm = main_tiles > 0 ? kMainUsPerK * k / spm * rounds(main_tiles * spm, cus) +
                                              reduce_us(main_tiles, spm, MainCfg::BM * MainCfg::BN)
                                        : 0.0;
       for (int sp = 1; sp <= 8; sp *= 2) {
         if (sp > 1 && (!allow_split || sp > max_split || tt == 0)) break;
+        if (!partial_ok(tt, sp, TailCfg::BM * TailCfg::BN)) break;
         const double ct = tt > 0 ? kTailUsPerK * k / sp * rounds(tt * sp, cus) +
                                        reduce_us(tt, sp, TailCfg::BM * TailCfg::BN)
                                  : 0.0;
