@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--pmc-mode", action="store_true",
                     help="for rocprofv3 --pmc: a few headline GEMV launches and one plain "
                          "512 MiB device copy (the byte-count calibration), then exit")
+    ap.add_argument("--pmc-gemm", action="store_true",
+                    help="for rocprofv3 --pmc: a few prefill GEMM launches, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the ROCmFP4 "
@@ -161,6 +163,17 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} CUs={props.multi_processor_count} lib={R.library_path()}")
+
+    if args.pmc_gemm:
+        wg_host, a_host, gcfg = synth.gemm_inputs("prefill")
+        wg = torch.from_numpy(wg_host).to(dev)
+        a = a_host.to(dev)
+        c = torch.empty((gcfg["m"], gcfg["n"]), dtype=torch.bfloat16, device=dev)
+        for _ in range(8):
+            R.rfp4_gemm(wg, gcfg["layout"], gcfg["n"], gcfg["k"], a, c)
+        torch.cuda.synchronize()
+        log("pmc gemm mode done: 8 prefill GEMM launches")
+        return
 
     # ---------------- headline: up-projection GEMV, dual, fp16, batch 1
     w_host, x_host, cfg = synth.gemv_inputs("up")
