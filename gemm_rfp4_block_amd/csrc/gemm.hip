@@ -117,24 +117,29 @@ using MainCfg = std::conditional_t<
     std::conditional_t<RFP4_GEMM_MAIN == 2, TileCfg<256, 256, 2, 2, RFP4_GEMM_MAIN_PD>,
                        std::conditional_t<RFP4_GEMM_PINGPONG != 0, TileCfg<256, 256, 4, 2, 2, true>,
                                           TileCfg<256, 256, 4, 2, RFP4_GEMM_MAIN_PD>>>>;
-// Tail tiles: 4 = 128 x 128, eight wavefronts (32 x 64 each) on the ping-pong schedule;
+// Tail tiles: 5 = 128 x 128, four wavefronts (64 x 64 each, one per SIMD): measured
+// against 4 (the ping-pong schedule, whose 32 x 64 wavefront tiles issue only 8 MFMAs
+// per phase; counters: MFMA busy 22 % of the time) 18-22 % faster on all-tail plans;
+// 4 = 128 x 128, eight wavefronts (32 x 64 each) on the ping-pong schedule;
 // 0 = 128 x 64, four wavefronts (64 x 32 each); 1 = 128 x 64, eight
 // wavefronts (32 x 32 each); 2 = 64 x 64, four wavefronts (32 x 32 each); 3 = 128 x 32,
-// four wavefronts (32 x 32 each). RFP4_GEMM_TAIL_PD: steps of A prefetched.
+// four wavefronts (32 x 32 each); 5 = 128 x 128, four wavefronts (64 x 64 each).
+// RFP4_GEMM_TAIL_PD: steps of A prefetched.
 #ifndef RFP4_GEMM_TAIL
-#define RFP4_GEMM_TAIL 4
+#define RFP4_GEMM_TAIL 5
 #endif
 #ifndef RFP4_GEMM_TAIL_PD
-#define RFP4_GEMM_TAIL_PD 2
+#define RFP4_GEMM_TAIL_PD 1
 #endif
 using TailCfg = std::conditional_t<
     RFP4_GEMM_TAIL == 4, TileCfg<128, 128, 4, 2, 2, true>,
+    std::conditional_t<RFP4_GEMM_TAIL == 5, TileCfg<128, 128, 2, 2, RFP4_GEMM_TAIL_PD>,
     std::conditional_t<
     RFP4_GEMM_TAIL == 1, TileCfg<128, 64, 4, 2, RFP4_GEMM_TAIL_PD>,
     std::conditional_t<
         RFP4_GEMM_TAIL == 2, TileCfg<64, 64, 2, 2, RFP4_GEMM_TAIL_PD>,
         std::conditional_t<RFP4_GEMM_TAIL == 3, TileCfg<128, 32, 4, 1, RFP4_GEMM_TAIL_PD>,
-                           TileCfg<128, 64, 2, 2, RFP4_GEMM_TAIL_PD>>>>>;
+                           TileCfg<128, 64, 2, 2, RFP4_GEMM_TAIL_PD>>>>>>;
 
 // LDS tiles are rows of 64 bf16 (128 bytes, eight 16-byte chunks); chunk c of row r
 // is stored at chunk position c ^ ((r >> 1) & 7). A 16-byte access by 16 lanes covers
@@ -818,7 +823,7 @@ hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint
 // partial sums at kReduceBytesPerUs plus kReduceFixedUs. It ranks the measured plans of
 // those shapes in the measured order of their best.
 constexpr double kMainUsPerK = 0.030;
-constexpr double kTailUsPerK = 0.012;
+constexpr double kTailUsPerK = 0.0102;
 constexpr double kPartialExp = 0.4;
 constexpr double kReduceBytesPerUs = 3.8e6;
 constexpr double kReduceFixedUs = 5.0;
