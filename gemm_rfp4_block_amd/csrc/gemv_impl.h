@@ -1,4 +1,6 @@
-// Fused dequant + GEMV for decode: y[b][r] = sum_c W[r][c] * x[b][c], batch 1..8.
+// Fused dequant + GEMV for decode: y[b][r] = sum_c W[r][c] * x[b][c], batch 1..8 (the
+// dot-product kernel; batches from 3 on default to the matrix-core kernel of
+// gemv_mfma.h).
 //
 // The page names gemv as the decode hot path ("Feasibility Report: Porting ROCmFP4
 // to Atlas", "Kernel System" and "Integration Options", Option 2) and says that on
@@ -22,15 +24,16 @@
 // the row groups, which its wavefronts take round-robin: every CU gets the same work.
 // Each lane keeps three units in flight.
 //
-// Arithmetic. Each block's 32 weights are decoded to f16/bf16 pairs (rfp4_decode.h)
-// and multiplied with the activations with v_dot2_f32_{f16,bf16}: one fp32 partial
-// sum per 16-weight half, then one fp32 FMA with that half's E4M3 scale. The partial
-// sums of the CL lanes of a row are combined with a butterfly of cross-lane shuffles
-// and the 1/2 of the half-scale is applied at the store.
+// Arithmetic. Each block's 32 weights are decoded to f16/bf16 pairs of unscaled codebook
+// values (f16: high-byte table plus zero-spread, below; bf16: E4M3 codes and the packed
+// FP8 conversion of rfp4_decode.h) and multiplied with the activations with
+// v_dot2_f32_{f16,bf16}: one fp32 partial sum per 16-weight half, then one fp32 FMA with
+// that half's E4M3 scale. The partial sums of the CL lanes of a row are combined with a
+// butterfly of cross-lane shuffles and the 1/2 of the half-scale is applied at the store.
 //
 // Activations are staged once per workgroup into LDS when they fit the budget (layout
-// at xs_index); otherwise they are read from global memory, where they stay
-// cache-resident.
+// at xs_index), with the first staging loads issued ahead of the first weight units;
+// otherwise they are read from global memory, where they stay cache-resident.
 
 #pragma once
 
