@@ -3,17 +3,27 @@
 //
 //   y[b][r] = sum_c weight(r, c) * x[b][c]
 //
-// Mapping. A workgroup of W wavefronts owns 16 consecutive weight rows (one MFMA tile
-// of v_mfma_f32_16x16x32_{f16,bf16}). Lane l of a wavefront serves as B-operand lane for
-// weight row l % 16 and as A-operand lane for activation row l % 16 (rows beyond the
-// batch read a clamped, finite row whose results are never stored); the lane group
-// l / 16 and the wavefront index pick which units of the row the lane streams: lane
-// group g = 4 w + l / 16 takes units g, g + 4W, g + 8W, ... (a unit is P = 1 or 2
-// consecutive blocks, loaded as in the dot-product kernel). The sum over k is order
-// free, so each MFMA adds, for every lane group, 8 consecutive weights of that lane's
-// own unit against the matching 8 activations: block j gives four MFMA steps s = 0..3
-// over weights 8s .. 8s+7 (low nibbles of qs words 0, 1 / 2, 3, then the high nibbles),
-// and the activation chunk of step s is the 16-byte unit s of the block.
+// Mapping. A workgroup of four wavefronts (one per SIMD) owns 16 consecutive weight
+// rows (one MFMA tile of v_mfma_f32_16x16x32_{f16,bf16}). Lane l of a wavefront serves
+// as B-operand lane for weight row l % 16 and as A-operand lane for activation row
+// l % 16 (rows beyond the batch read a clamped, finite row whose results are never
+// stored); the lane group g = 4 w + l / 16 (w the wavefront) takes units g, g + 16,
+// g + 32, ... of the row (a unit is P = 1 or 2 consecutive blocks, loaded as in the
+// dot-product kernel). The sum over k is order free, so each MFMA adds, for every lane
+// group, 8 consecutive weights of that lane's own unit against the matching 8
+// activations: block j gives four MFMA steps s = 0..3 over weights 8s .. 8s+7 (low
+// nibbles of qs words 0, 1 / 2, 3, then the high nibbles), and the activations of step
+// s are the 16-byte piece s of the block.
+//
+// Activations. The 16 lane groups consume the units of a row in chunks of 16 (chunk
+// t = units 16t .. 16t + 15). Each chunk's activations, for all batch rows, are staged
+// in LDS just before it is multiplied; the loads are issued three chunks ahead into
+// registers, together with the weights of the same chunk, so that the staging waits
+// only for loads that are due anyway. Per chunk the workgroup reads batch x 16 units of
+// activations from the L2; staging the whole activation matrix up front, or having
+// every lane read its activations from global memory, measured 1.2 to 1.6 times slower.
+// Four wavefronts per workgroup measured faster than 8 or 16 on every decode shape
+// (smaller barriers, registers for three chunks in flight) and faster than 2.
 //
 // Decode. Each workgroup builds a 128-entry LDS table: for every value of a scale byte's
 // low seven bits, the f16 (or bf16) encodings of the eight magnitudes times the decoded
@@ -23,7 +33,7 @@
 // interleaving v_perm_b32; the scale is part of the table, so the MFMA products are the
 // exact weight times activation products, summed in fp32.
 //
-// The W wavefronts' 16 x 16 accumulator tiles are added in LDS in a fixed order and
+// The four wavefronts' 16 x 16 accumulator tiles are added in LDS in a fixed order and
 // the batch rows are stored.
 
 #pragma once
@@ -84,23 +94,28 @@ __device__ __forceinline__ void unit_scale_bytes(const UnitRaw<P>& u, uint32_t& 
   e1 = LAYOUT == kDual ? (word >> 8) & 0x7Fu : e0;
 }
 
-template <int LAYOUT, int XT, int P, bool XLDS, int W, int NP>
-__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvParts<NP> parts, int nu,
+constexpr int kMfmaWaves = 4;
+
+template <int LAYOUT, int XT, int P, bool BIG, int NP>
+__global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvParts<NP> parts, int nu,
                                                            const uint16_t* __restrict__ x,
                                                            int64_t ldx, int batch) {
+  constexpr int W = kMfmaWaves;
   constexpr int UB = P * block_bytes(LAYOUT);
   constexpr int THREADS = 64 * W;
+  constexpr int G = 4 * W;        // lane groups: units of a row per chunk
+  constexpr int PU = 4 * P;       // 16-byte activation pieces per unit
+  constexpr int XPT = BIG ? 2 * P : P;  // pieces per thread per chunk: batch <= 8 or <= 4
   typedef MfmaOps<XT> M;
   extern __shared__ uint4 smem_m[];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // weight row of the tile (B) and activation row (A)
-  const int g = 4 * wv + (lane >> 4);  // lane group: units g, g + 4W, ...
-  const int xrows = XLDS ? batch * nu * (4 * P + 1) : 0;  // 16-byte LDS units of x
-  uint4* const xs = smem_m;
-  uint4* const lut = smem_m + xrows;
-  mf32x4* const red = reinterpret_cast<mf32x4*>(lut + 128);
+  const int g = 4 * wv + (lane >> 4);  // lane group: unit g of each chunk
+  uint4* const lut = smem_m;
+  uint4* const xs = smem_m + 128;  // chunk: batch x G units x (PU + 1) pieces
+  mf32x4* const red = reinterpret_cast<mf32x4*>(xs);  // reused after the last chunk
 
   // Part and row of this workgroup's tile.
   const int tile = blockIdx.x;
@@ -113,10 +128,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvParts<NP> p
   const uint8_t* const wrow =
       (NP > 1 ? parts.w[mi] : parts.w[0]) + static_cast<int64_t>(min(r0 + col, n_part - 1)) * rowbytes;
 
-  // Units of this lane: u(t) = g + 4W t, t < T; past the row end the address is clamped
-  // and the weights are zeroed.
-  const int T = (nu + 4 * W - 1) / (4 * W);
-  auto unit_ptr = [&](int t) { return wrow + static_cast<int64_t>(min(g + 4 * W * t, nu - 1)) * UB; };
+  // Chunk t covers units G t .. G t + G - 1 of every row: lane group g takes unit
+  // G t + g. Past the row end the address is clamped and the weights are zeroed.
+  const int T = (nu + G - 1) / G;
+  auto unit_ptr = [&](int t) { return wrow + static_cast<int64_t>(min(G * t + g, nu - 1)) * UB; };
 
   // Decode table (threads 0..127).
   if (threadIdx.x < 128) {
@@ -132,46 +147,53 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvParts<NP> p
     lut[threadIdx.x] = uint4{lo[0], lo[1], hi[0], hi[1]};
   }
 
-  // Activations: the first loads are issued before the weight units so that the LDS
-  // stores wait only for them.
+  // Activation chunk t: piece i = (b G + u) PU + p is the 16-byte piece p of unit G t + u
+  // of activation row b (clamped to the last unit), stored at LDS unit
+  // (b G + u)(PU + 1) + p; consecutive threads read consecutive pieces of a row. The
+  // loads are clamped to the last piece, so every thread loads XPT pieces in bounds.
+  const int pieces = batch * G * PU;
+  struct XChunk {
+    uint4 v[XPT];
+  };
+  auto x_load = [&](int t) {
+    XChunk c;
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = min(static_cast<int>(threadIdx.x) + j * THREADS, pieces - 1);
+      const int p = i % PU;
+      const int bu = i / PU;
+      const int b = bu / G;
+      const int unit = min(G * t + (bu % G), nu - 1);
+      c.v[j] = *reinterpret_cast<const uint4*>(x + b * ldx + 32 * P * unit + 8 * p);
+    }
+    return c;
+  };
+  auto x_store = [&](XChunk c) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = static_cast<int>(threadIdx.x) + j * THREADS;
+      if (i < pieces) xs[(i / PU) * (PU + 1) + i % PU] = c.v[j];
+    }
+  };
+
+  // Three chunks in flight: the activations of chunk t are loaded just before its
+  // weights, so the LDS store of chunk t waits for exactly those loads and leaves the
+  // weights of chunk t (and later) in flight.
+  XChunk xr[3];
   UnitRaw<P> rb[3];
-  if constexpr (XLDS) {
-    const int units = batch * 4 * nu * P;
-    auto src_of = [&](int t) {
-      const int cc = t & 3;
-      const int jb = t >> 2;
-      const int b = jb / (nu * P);
-      const int j = jb - b * nu * P;
-      return reinterpret_cast<const uint4*>(x + b * ldx + 32 * j + 8 * cc);
-    };
-    auto dst_of = [&](int t) {
-      const int cc = t & 3;
-      const int jb = t >> 2;
-      const int b = jb / (nu * P);
-      const int j = jb - b * nu * P;
-      return xs + xs_index<P>(b, j / P, nu, j % P, cc);
-    };
-    const int t0 = threadIdx.x;
-    const uint4 v0 = *src_of(min(t0, units - 1));
-    const uint4 v1 = *src_of(min(t0 + THREADS, units - 1));
 #pragma unroll
-    for (int d = 0; d < 3; ++d) load_unit<LAYOUT, P>(unit_ptr(d), rb[d]);
-    if (t0 < units) *dst_of(t0) = v0;
-    if (t0 + THREADS < units) *dst_of(t0 + THREADS) = v1;
-    for (int t = t0 + 2 * THREADS; t < units; t += THREADS) *dst_of(t) = *src_of(t);
-  } else {
-#pragma unroll
-    for (int d = 0; d < 3; ++d) load_unit<LAYOUT, P>(unit_ptr(d), rb[d]);
+  for (int d = 0; d < 3; ++d) {
+    const int tc = min(d, T - 1);  // straight-line loads; a chunk past T is never used
+    xr[d] = x_load(tc);
+    load_unit<LAYOUT, P>(unit_ptr(tc), rb[d]);
   }
-  __syncthreads();
 
   const int xb = min(col, batch - 1);  // activation row of this A lane (clamped)
   mf32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
   auto consume = [&](const UnitRaw<P>& u, int t) {
-    const int uidx = g + 4 * W * t;
-    const bool valid = uidx < nu;
-    const int uc = min(uidx, nu - 1);
+    const bool valid = G * t + g < nu;
+    const uint4* const xu = xs + (xb * G + g) * (PU + 1);
     auto block = [&](auto b_c) {
       constexpr int B = decltype(b_c)::value;
       uint4 q = unit_qs<LAYOUT, P, B>(u);
@@ -180,12 +202,6 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvParts<NP> p
       unit_scale_bytes<LAYOUT, P, B>(u, e0, e1);
       const uint4 t0 = lut[e0];
       const uint4 t1 = LAYOUT == kDual ? lut[e1] : t0;
-      auto xop = [&](int s) -> uint4 {
-        if constexpr (XLDS)
-          return xs[xs_index<P>(xb, uc, nu, B, s)];
-        else
-          return *reinterpret_cast<const uint4*>(x + xb * ldx + 32 * (P * uc + B) + 8 * s);
-      };
       const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -198,37 +214,56 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvParts<NP> p
           pa = decode_plane((qa >> 4) & 0x07070707u, qa & 0x80808080u, t1);
           pb = decode_plane((qb >> 4) & 0x07070707u, qb & 0x80808080u, t1);
         }
-        acc = M::mfma(xop(s), uint4{pa.x, pa.y, pb.x, pb.y}, acc);
+        acc = M::mfma(xu[4 * B + s], uint4{pa.x, pa.y, pb.x, pb.y}, acc);
       }
     };
     block(std::integral_constant<int, 0>{});
     if constexpr (P == 2) block(std::integral_constant<int, 1>{});
   };
 
-  for (int t = 0; t < T; t += 3) {
+  // Per chunk: wait until every wavefront is done with the previous chunk, store this
+  // one, wait until it is complete, multiply; then issue chunk t + 3. Rounds of three
+  // chunks keep the register rings indexed by constants. Every round but the last
+  // loads unconditionally (clamped to the last chunk), since a path that skipped loads
+  // would make the compiler's load waits count the shortest path; the last round loads
+  // nothing and skips the chunks past T, so no load outlives the last multiply. The
+  // first barrier also orders the table writes before their first reads.
+  int t = 0;
+  for (; t + 3 < T; t += 3) {
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
-      if (d == 0 || t + d < T) {
-        consume(rb[d], t + d);
-        if (t + d + 3 < T) load_unit<LAYOUT, P>(unit_ptr(t + d + 3), rb[d]);
-      }
+      if (t + d > 0) __syncthreads();
+      x_store(xr[d]);
+      __syncthreads();
+      consume(rb[d], t + d);
+      const int tn = min(t + d + 3, T - 1);
+      xr[d] = x_load(tn);
+      load_unit<LAYOUT, P>(unit_ptr(tn), rb[d]);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    if (t + d < T) {
+      if (t + d > 0) __syncthreads();
+      x_store(xr[d]);
+      __syncthreads();
+      consume(rb[d], t + d);
     }
   }
 
   // Lane l, register i holds batch row 4 (l / 16) + i of weight row l % 16.
   float* const y = NP > 1 ? parts.y[mi] : parts.y[0];
   const int64_t ldy = NP > 1 ? parts.ldy[mi] : parts.ldy[0];
-  if constexpr (W > 1) {
-    red[wv * 64 + lane] = acc;
-    __syncthreads();
-    if (wv != 0) return;
-    for (int w = 1; w < W; ++w) {
-      const mf32x4 o = red[w * 64 + lane];
-      acc[0] += o[0];
-      acc[1] += o[1];
-      acc[2] += o[2];
-      acc[3] += o[3];
-    }
+  __syncthreads();  // the last chunk's reads are done before its LDS is reused
+  red[wv * 64 + lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+  for (int w = 1; w < W; ++w) {
+    const mf32x4 o = red[w * 64 + lane];
+    acc[0] += o[0];
+    acc[1] += o[1];
+    acc[2] += o[2];
+    acc[3] += o[3];
   }
   const int row = r0 + col;
   if (row < n_part) {
@@ -241,49 +276,35 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvParts<NP> p
 }
 
 struct MfmaPlan {
-  int p, nu, w, tiles;
-  bool xlds;
+  int p, nu, tiles;
+  bool big;
   size_t shm;
 };
 
-// Wavefronts per workgroup: the most (up to 16) that keep the launch within about 24
-// wavefronts per CU and give every lane group at least one unit.
+// LDS of a launch: the table plus one activation chunk (or the cross-wavefront sums,
+// if larger).
+inline size_t mfma_lds(int p, int batch) {
+  const size_t chunk = static_cast<size_t>(batch) * 4 * kMfmaWaves * (4 * p + 1) * 16;
+  const size_t red = static_cast<size_t>(kMfmaWaves) * 64 * 16;
+  return 128 * 16 + (chunk > red ? chunk : red);
+}
+
 inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch) {
   MfmaPlan pl;
   pl.p = nb % 2 == 0 ? 2 : 1;
   pl.nu = nb / pl.p;
   pl.tiles = 0;
   for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 15) / 16);
-  const int64_t target = 24LL * device_cu_count();
-  pl.w = 4;
-  for (int w = 16; w >= 8; w /= 2) {
-    if (static_cast<int64_t>(pl.tiles) * w <= target && 4 * w <= pl.nu) {
-      pl.w = w;
-      break;
-    }
-  }
-  const size_t xbytes = static_cast<size_t>(batch) * pl.nu * (4 * pl.p + 1) * 16;
-  const size_t fixed = 128 * 16 + static_cast<size_t>(pl.w) * 64 * 16;
-  pl.xlds = xbytes + fixed <= 64 * 1024;
-  pl.shm = (pl.xlds ? xbytes : 0) + fixed;
+  pl.big = batch > 4;
+  pl.shm = mfma_lds(pl.p, batch);
   return pl;
 }
 
-template <int LAYOUT, int XT, int P, bool XLDS, int NP>
-hipError_t launch_mfma_w(const MfmaPlan& pl, const GemvParts<NP>& gp, const uint16_t* x, int64_t ldx,
+template <int LAYOUT, int XT, int P, bool BIG, int NP>
+hipError_t launch_mfma_p(const MfmaPlan& pl, const GemvParts<NP>& gp, const uint16_t* x, int64_t ldx,
                          int batch, hipStream_t stream) {
-  const dim3 grid(pl.tiles), block(64 * pl.w);
-  switch (pl.w) {
-    case 16:
-      gemv_mfma_kernel<LAYOUT, XT, P, XLDS, 16, NP><<<grid, block, pl.shm, stream>>>(gp, pl.nu, x, ldx, batch);
-      break;
-    case 8:
-      gemv_mfma_kernel<LAYOUT, XT, P, XLDS, 8, NP><<<grid, block, pl.shm, stream>>>(gp, pl.nu, x, ldx, batch);
-      break;
-    default:
-      gemv_mfma_kernel<LAYOUT, XT, P, XLDS, 4, NP><<<grid, block, pl.shm, stream>>>(gp, pl.nu, x, ldx, batch);
-      break;
-  }
+  gemv_mfma_kernel<LAYOUT, XT, P, BIG, NP><<<dim3(pl.tiles), dim3(64 * kMfmaWaves), pl.shm, stream>>>(
+      gp, pl.nu, x, ldx, batch);
   return hipGetLastError();
 }
 
@@ -302,20 +323,21 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
     gp.gbeg[i + 1] = gp.gbeg[i] + static_cast<int>((parts[i].n + 15) / 16);
   }
   if (pl.p == 2)
-    return pl.xlds ? launch_mfma_w<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, stream)
-                   : launch_mfma_w<LAYOUT, XT, 2, false, NP>(pl, gp, x, ldx, batch, stream);
-  return pl.xlds ? launch_mfma_w<LAYOUT, XT, 1, true, NP>(pl, gp, x, ldx, batch, stream)
-                 : launch_mfma_w<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, stream);
+    return pl.big ? launch_mfma_p<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, stream)
+                  : launch_mfma_p<LAYOUT, XT, 2, false, NP>(pl, gp, x, ldx, batch, stream);
+  return pl.big ? launch_mfma_p<LAYOUT, XT, 1, true, NP>(pl, gp, x, ldx, batch, stream)
+                : launch_mfma_p<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, stream);
 }
 
 // Matrix-core path for the batches where it is faster: measured on the decode shapes,
-// the dot-product kernel wins at batch 1 (its decode needs no table and no cross-wave
-// reduction), the two tie at batch 2, and the matrix cores win from batch 4 on (the
-// dot-product work grows with the batch, the decode here does not; 3.7x at batch 8).
-// The environment variable RFP4_GEMV_MFMA = "0" selects the dot-product kernel and "1"
-// the matrix cores for every batch; otherwise batches >= RFP4_GEMV_MFMA_MIN_BATCH.
+// the dot-product kernel wins at batch 1 (12.5 against 14.7 us at 17408 x 5120: its
+// decode needs no table, no staging and no cross-wave reduction) and the matrix cores
+// from batch 2 on (15.7 against 16.6 us there; the dot-product work grows with the
+// batch, the decode here does not). The environment variable RFP4_GEMV_MFMA = "0"
+// selects the dot-product kernel and "1" the matrix cores for every batch; otherwise
+// batches >= RFP4_GEMV_MFMA_MIN_BATCH take the matrix cores.
 #ifndef RFP4_GEMV_MFMA_MIN_BATCH
-#define RFP4_GEMV_MFMA_MIN_BATCH 3
+#define RFP4_GEMV_MFMA_MIN_BATCH 2
 #endif
 inline bool use_mfma(int batch) {
   const char* env = getenv("RFP4_GEMV_MFMA");

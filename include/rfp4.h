@@ -114,9 +114,9 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * Options", Option 2): for b < batch and r < n,
  *   y[b * ldy + r] = sum_c weight(r, c) * x[b * ldx + c]
  * with x of dtype xdtype (RFP4_F16 or RFP4_BF16), products formed exactly and summed
- * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n. Batches 1 and 2
- * run a dot-product kernel, batches from 3 on a matrix-core kernel (the summation
- * order, hence the last bits, differ between the two); the environment variable
+ * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n. Batch 1 runs a
+ * dot-product kernel, batches from 2 on a matrix-core kernel (the summation order,
+ * hence the last bits, differ between the two); the environment variable
  * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. */
 RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const void* x,
                       int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,

@@ -742,6 +742,10 @@ MFMA_CASES = [  # layout, n, k, batch, dtype
     (0, 1, 256, 1, "f16"), (1, 7, 512, 2, "bf16"), (0, 33, 1408, 4, "f16"), (1, 45, 1056, 6, "bf16"),
     (0, 130, 96, 7, "f16"), (1, 17, 32, 8, "bf16"), (0, 300, 4000, 8, "bf16"), (1, 64, 99968, 2, "f16"),
     (0, 999, 2304, 8, "f16"),
+    # chunks of 16 units per row: 4 (T % 3 == 1), 7 with a ragged last chunk, 6 with
+    # single-block units and a ragged last chunk, 6 exactly at batch 4
+    (0, 200, 4096, 4, "f16"), (1, 77, 6912, 5, "bf16"), (0, 50, 2720, 6, "bf16"),
+    (1, 5120, 6144, 4, "bf16"),
 ]
 
 
