@@ -244,7 +244,7 @@ __device__ __forceinline__ void unit_scales(const UnitRaw<P>& u, float& s0, floa
 // `xunit(b, cc)` returns the 16-byte activation unit cc (values 8cc..8cc+7 of the
 // block) of activation row b. Each half's dot product is split over two chains.
 template <int XT, int BATCH, typename XUnit>
-__device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, XUnit xunit,
+__device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, bool valid, XUnit xunit,
                                           float (&acc)[BATCH]) {
   typedef Act<XT> A;
   typedef typename A::pair pair;
@@ -285,8 +285,10 @@ __device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, XUnit xu
       p2 = A::dot(wl[t + 4], x0[t + 4], p2);
       p3 = A::dot(wh[t + 4], x1[t + 4], p3);
     }
-    acc[b] = __builtin_fmaf(s0, p0 + p2, acc[b]);
-    acc[b] = __builtin_fmaf(s1, p1 + p3, acc[b]);
+    // A masked lane adds nothing: its products may be 0 * inf = NaN, so they are
+    // dropped, not scaled by zero.
+    acc[b] = __builtin_fmaf(s0, valid ? p0 + p2 : 0.f, acc[b]);
+    acc[b] = __builtin_fmaf(s1, valid ? p1 + p3 : 0.f, acc[b]);
   }
 }
 
@@ -308,17 +310,15 @@ __device__ __forceinline__ void unit_block(const UnitRaw<P>& u, const uint4* xu,
                                            float (&acc)[BATCH]) {
   float s0, s1;
   unit_scales<LAYOUT, P, B>(u, s0, s1);
-  // A lane past the end of a ragged row re-reads the row's last unit; a zero scale
-  // makes its contribution vanish.
-  s0 = valid ? s0 : 0.f;
-  s1 = valid ? s1 : 0.f;
+  // A lane past the end of a ragged row re-reads the row's last unit (weights and
+  // activations); block_dot drops its contribution.
   auto xunit = [&](int b, int cc) -> uint4 {
     if constexpr (XLDS)
       return xu[b * xrow + 4 * B + cc];
     else
       return *reinterpret_cast<const uint4*>(xg + b * ldx + 32 * B + 8 * cc);
   };
-  block_dot<XT, BATCH>(unit_qs<LAYOUT, P, B>(u), s0, s1, xunit, acc);
+  block_dot<XT, BATCH>(unit_qs<LAYOUT, P, B>(u), s0, s1, valid, xunit, acc);
 }
 
 // The matrices of one launch (up to kMaxGemvParts, sharing k and the activations):

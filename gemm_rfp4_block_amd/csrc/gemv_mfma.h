@@ -148,9 +148,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   }
 
   // Activation chunk t: piece i = (b G + u) PU + p is the 16-byte piece p of unit G t + u
-  // of activation row b (clamped to the last unit), stored at LDS unit
-  // (b G + u)(PU + 1) + p; consecutive threads read consecutive pieces of a row. The
-  // loads are clamped to the last piece, so every thread loads XPT pieces in bounds.
+  // of activation row b, stored at LDS unit (b G + u)(PU + 1) + p; consecutive threads
+  // read consecutive pieces of a row. The loads are clamped to the last piece (and to
+  // the row's last unit), so every thread loads XPT pieces in bounds; pieces of units
+  // past the row end are zeroed, so the zeroed weights there meet zeros (0 * inf would
+  // be NaN).
   const int pieces = batch * G * PU;
   struct XChunk {
     uint4 v[XPT];
@@ -163,8 +165,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
       const int p = i % PU;
       const int bu = i / PU;
       const int b = bu / G;
-      const int unit = min(G * t + (bu % G), nu - 1);
-      c.v[j] = *reinterpret_cast<const uint4*>(x + b * ldx + 32 * P * unit + 8 * p);
+      const int unit = G * t + (bu % G);
+      const uint4 v = *reinterpret_cast<const uint4*>(x + b * ldx + 32 * P * min(unit, nu - 1) + 8 * p);
+      c.v[j] = unit < nu ? v : uint4{0u, 0u, 0u, 0u};
     }
     return c;
   };
@@ -191,13 +194,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   const int xb = min(col, batch - 1);  // activation row of this A lane (clamped)
   mf32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  auto consume = [&](const UnitRaw<P>& u, int t) {
-    const bool valid = G * t + g < nu;
+  // A lane group past the row end holds the row's last unit of weights against zeroed
+  // activations, so it adds zeros.
+  auto consume = [&](const UnitRaw<P>& u) {
     const uint4* const xu = xs + (xb * G + g) * (PU + 1);
     auto block = [&](auto b_c) {
       constexpr int B = decltype(b_c)::value;
-      uint4 q = unit_qs<LAYOUT, P, B>(u);
-      if (!valid) q = uint4{0u, 0u, 0u, 0u};
+      const uint4 q = unit_qs<LAYOUT, P, B>(u);
       uint32_t e0, e1;
       unit_scale_bytes<LAYOUT, P, B>(u, e0, e1);
       const uint4 t0 = lut[e0];
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
       if (t + d > 0) __syncthreads();
       x_store(xr[d]);
       __syncthreads();
-      consume(rb[d], t + d);
+      consume(rb[d]);
       const int tn = min(t + d + 3, T - 1);
       xr[d] = x_load(tn);
       load_unit<LAYOUT, P>(unit_ptr(tn), rb[d]);
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
       if (t + d > 0) __syncthreads();
       x_store(xr[d]);
       __syncthreads();
-      consume(rb[d], t + d);
+      consume(rb[d]);
     }
   }
 

@@ -271,6 +271,43 @@ def test_gemv_multi_equals_single_calls(monkeypatch):
         assert torch.equal(y, s1)
 
 
+NONFINITE_X = [  # kernel, plan, layout, n, k, batch, dtype
+    ("0", "2:32", 1, 40, 17408, 2, "bf16"),  # dot product, 272 units over 32 lanes: ragged
+    ("0", "1:64", 0, 21, 4000, 1, "f16"),    # dot product, 125 single blocks over 64 lanes
+    ("1", None, 0, 33, 1408, 3, "f16"),      # matrix cores, 22 units: last chunk 6 of 16
+    ("1", None, 1, 45, 1056, 8, "bf16"),     # matrix cores, 33 single blocks
+]
+
+
+@pytest.mark.parametrize("case", NONFINITE_X, ids=lambda c: "mfma{}-{}-L{}n{}k{}b{}{}".format(*c))
+def test_gemv_nonfinite_activations(case, monkeypatch):
+    """An infinite activation in the last block of a row: rows whose exact sum is +-inf
+    (or NaN, where a zero weight meets it) give exactly that; lanes or lane groups past
+    the row end, which re-read that last block, must add nothing (not 0 * inf = NaN).
+    Other activation rows stay finite and within tolerance."""
+    mode, plan, layout, n, k, batch, dt = case
+    monkeypatch.setenv("RFP4_GEMV_MFMA", mode)
+    if plan is not None:
+        monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
+    rng = np.random.default_rng(9300 + n + k)
+    w = synth.weights(rng, layout, n, k)
+    x = synth.activations(rng, batch, k, dt)
+    x[0, k - 1] = float("inf")
+    if batch > 2:
+        x[2, k - 33] = float("-inf")
+    y = R.rfp4_gemv(dev(w), layout, n, k, x.to(DEV).contiguous()).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore"):  # 0 * inf in the exact sums
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
+    nonfinite = ~np.isfinite(y_ref)
+    assert nonfinite[0].all()
+    assert np.array_equal(np.isnan(y), np.isnan(y_ref))
+    assert np.array_equal(y[nonfinite & ~np.isnan(y_ref)], y_ref[nonfinite & ~np.isnan(y_ref)])
+    rows = np.isfinite(y_ref).all(axis=1)
+    if rows.any():
+        assert O.normalized_error(y[rows], y_ref[rows], den[rows]) <= TOL
+
+
 def test_gemv_zero_scales_give_zero():
     rng = np.random.default_rng(31)
     n, k = 64, 1024
