@@ -274,6 +274,7 @@ def test_gemv_multi_equals_single_calls(monkeypatch):
 NONFINITE_X = [  # kernel, plan, layout, n, k, batch, dtype
     ("0", "2:32", 1, 40, 17408, 2, "bf16"),  # dot product, 272 units over 32 lanes: ragged
     ("0", "1:64", 0, 21, 4000, 1, "f16"),    # dot product, 125 single blocks over 64 lanes
+    ("0", "1:64", 1, 40, 17408, 8, "bf16"),  # dot product, activations from global memory
     ("1", None, 0, 33, 1408, 3, "f16"),      # matrix cores, 22 units: last chunk 6 of 16
     ("1", None, 1, 45, 1056, 8, "bf16"),     # matrix cores, 33 single blocks
 ]
