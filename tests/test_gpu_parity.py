@@ -836,3 +836,54 @@ def test_gemv_mfma_zero_scales_give_zero(monkeypatch):
     x = synth.activations(np.random.default_rng(9301), batch, k, "bf16")
     y = run_gemv(w.reshape(n, -1), layout, n, k, x)
     assert np.all(y == 0.0)
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_replay_matches_eager(monkeypatch):
+    """Every entry point captured into one HIP graph (batch-1 and batch-4 GEMV, a GEMM
+    with split k, dequant, encoder) and replayed three times, with eager work between
+    the replays, gives exactly the eager results. The GEMM runs eagerly first so that
+    its workspace exists before the capture, as the header asks."""
+    monkeypatch.setenv("RFP4_GEMM_PLAN", "tail2")
+    rng = np.random.default_rng(9500)
+    layout, n, k = 0, 1040, 2048
+    wd = dev(synth.weights(rng, layout, n, k))
+    x1 = synth.activations(rng, 1, k, "f16").to(DEV).contiguous()
+    x4 = synth.activations(rng, 4, k, "bf16").to(DEV).contiguous()
+    a = synth.activations(rng, 200, k, "bf16").to(DEV).contiguous()
+    src = synth.real_weights(rng, 96, k, "bf16").to(DEV).contiguous()
+
+    outs = {"y1": torch.empty((1, n), dtype=torch.float32, device=DEV),
+            "y4": torch.empty((4, n), dtype=torch.float32, device=DEV),
+            "c": torch.empty((200, n), dtype=torch.bfloat16, device=DEV),
+            "d": torch.empty((n, k), dtype=torch.float32, device=DEV),
+            "q": torch.empty((96, R.rfp4_row_bytes(layout, k)), dtype=torch.uint8, device=DEV)}
+
+    def run():
+        R.rfp4_gemv(wd, layout, n, k, x1, y=outs["y1"])
+        R.rfp4_gemv(wd, layout, n, k, x4, y=outs["y4"])
+        R.rfp4_gemm(wd, layout, n, k, a, c=outs["c"])
+        R.rfp4_dequant(wd, layout, n, k, out=outs["d"])
+        R.rfp4_quantize(src, layout, out=outs["q"])
+
+    run()
+    torch.cuda.synchronize()
+    eager = {key: v.clone() for key, v in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm-up on the capture stream (its GEMM workspace)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key, v in outs.items():
+            assert torch.equal(v, eager[key]), (key, rep)
