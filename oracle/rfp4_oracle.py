@@ -42,15 +42,16 @@ taken here (each also listed with its reason in the design notes):
   R-QUANT the encoder (``quantize``): smallest finite half-scale reaching the group's
           largest magnitude with code 10, then the nearest codebook entry, ties to the
           smaller magnitude. The page gives no encoder; pinned by the decode round trip
-          and by brute-force nearest-entry and minimal-scale checks.
+          and by brute-force nearest-entry and minimal-scale checks. [parity unpinned]
 
 Pins (tests under tests/ marked "not gpu"): the printed block sizes and bits per
 weight, the printed codebook, E4M3 on all 256 bytes against the textbook closed form
 and against torch's float8_e4m3fn, exact rational brute force on tiny matrices, the
 special cases that reduce to an integer matrix product, and exact invariants (sign
-flip, exponent step, dual == fast when both halves share a scale). The two readings
-marked "parity unpinned" cannot be checked against the page; they are pinned only
-to their own stated convention through a witness block.
+flip, exponent step, dual == fast when both halves share a scale). The three readings
+marked "parity unpinned" cannot be checked against the page: R-NIB and R-HALF are
+pinned only to their own stated convention through witness blocks, R-QUANT to its
+stated rule by exact brute force.
 """
 
 from __future__ import annotations
