@@ -9,8 +9,9 @@ from the 256 MB Infinity Cache. The K steps are captured once in a HIP graph and
 replayed inside the timed region, bracketed by device synchronizations.
 
 Also measured in the same run (reported under "gemm" and "extra"): the prefill GEMM
-(2048 x 17408 x 5120, bf16, TFLOP/s), the fast-layout down-projection GEMV at batch
-1/2/4/8 (bf16), dequantization, and the 64-layer decode sweep (448 GEMVs, 12.3 GB).
+(2048 x 17408 x 5120, bf16, TFLOP/s), the up-projection GEMV at batch 2/4/8 (matrix
+cores), the fast-layout down-projection GEMV at batch 1/2/4/8 (bf16), dequantization,
+encoding, and the 64-layer decode sweep (448 GEMVs, 12.3 GB).
 Per-kernel durations come from HIP events recorded around every launch on the stream
 the kernel runs on. The CPU baseline times the fp64 oracle on the host.
 
@@ -239,6 +240,20 @@ def main():
     extra = {"gemv_up_graph_replay_matches_eager": replay_ok,
              "gemv_up_direct_launches": {"us_per_launch": round(direct_us, 3),
                                          "GB/s": round(alg_bytes / (direct_us * 1e-6) / 1e9, 1)}}
+    # ---------------- up-projection GEMV at batch 2/4/8 (the matrix-core kernel)
+    xs_host = synth.activations(np.random.default_rng(11), 8, k, "f16")
+    up_batched = {}
+    for b in (2, 4, 8):
+        xb = xs_host[:b].contiguous().to(dev)
+        yb = torch.empty((b, n), dtype=torch.float32, device=dev)
+        for i in range(10):
+            R.rfp4_gemv(copies[i % nc], layout, n, k, xb, yb)
+        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemv(copies[i % nc], layout, n, k, xb, yb), 100))
+        bts = w_bytes + b * k * 2 + b * n * 4
+        up_batched[f"b{b}"] = {"GB/s": round(bts / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": bts,
+                               **{kk: round(v, 2) for kk, v in d.items()}}
+        log(f"gemv up b={b}: mean {d['mean_us']:.2f} us -> {up_batched[f'b{b}']['GB/s']:.0f} GB/s")
+    extra["gemv_up_dual_f16_batched"] = up_batched
     del copies
     torch.cuda.empty_cache()
 
