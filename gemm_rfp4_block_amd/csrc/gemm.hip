@@ -906,55 +906,6 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
   return best;
 }
 
-// Workspace for split partial sums, one per (device, stream) so that calls ordered on a
-// stream reuse it and calls on different streams never share it. It grows on demand
-// (after the stream's earlier work has finished) and is kept until the process ends.
-hipError_t split_workspace(hipStream_t stream, size_t bytes, float** out) {
-  struct Entry {
-    int dev;
-    hipStream_t stream;
-    void* ptr;
-    size_t bytes;
-  };
-  static std::mutex mu;
-  static Entry entries[256];
-  static int count = 0;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  Entry* en = nullptr;
-  for (int i = 0; i < count; ++i)
-    if (entries[i].dev == dev && entries[i].stream == stream) en = &entries[i];
-  if (en == nullptr) {
-    if (count == 256) return hipErrorOutOfMemory;
-    en = &entries[count++];
-    *en = Entry{dev, stream, nullptr, 0};
-  }
-  if (en->bytes < bytes) {
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cap);
-    if (e != hipSuccess) return e;
-    if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
-    if (en->ptr != nullptr) {
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return e;
-      e = hipFree(en->ptr);
-      en->ptr = nullptr;
-      en->bytes = 0;
-      if (e != hipSuccess) return e;
-    }
-    e = hipMalloc(&en->ptr, bytes);
-    if (e != hipSuccess) {
-      en->ptr = nullptr;
-      return e;
-    }
-    en->bytes = bytes;
-  }
-  *out = static_cast<float*>(en->ptr);
-  return hipSuccess;
-}
-
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
@@ -981,7 +932,8 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
                                               : 0;
     if (main_bytes + tail_bytes > 0) {
       float* ws = nullptr;
-      if (split_workspace(stream, main_bytes + tail_bytes, &ws) != hipSuccess) {
+      if (stream_workspace(kWorkspaceGemm, stream, main_bytes + tail_bytes, reinterpret_cast<void**>(&ws)) !=
+          hipSuccess) {
         (void)hipGetLastError();  // clear a failed allocation; run every tile unsplit
         plan.splits = 1;
         plan.main_splits = 1;

@@ -34,7 +34,9 @@
 // exact weight times activation products, summed in fp32.
 //
 // The four wavefronts' 16 x 16 accumulator tiles are added in LDS in a fixed order and
-// the batch rows are stored.
+// the batch rows are stored. Long rows on few tiles split each tile's chunks between
+// two workgroups (see mfma_splits); the last of them to finish adds both parts in a
+// fixed order.
 
 #pragma once
 
@@ -99,7 +101,9 @@ constexpr int kMfmaWaves = 4;
 template <int LAYOUT, int XT, int P, bool BIG, int NP>
 __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvParts<NP> parts, int nu,
                                                            const uint16_t* __restrict__ x,
-                                                           int64_t ldx, int batch) {
+                                                           int64_t ldx, int batch, int splits,
+                                                           float* __restrict__ partial,
+                                                           int* __restrict__ arrivals) {
   constexpr int W = kMfmaWaves;
   constexpr int UB = P * block_bytes(LAYOUT);
   constexpr int THREADS = 64 * W;
@@ -117,8 +121,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   uint4* const xs = smem_m + 128;  // chunk: batch x G units x (PU + 1) pieces
   mf32x4* const red = reinterpret_cast<mf32x4*>(xs);  // reused after the last chunk
 
-  // Part and row of this workgroup's tile.
-  const int tile = blockIdx.x;
+  // Tile and part of this workgroup: the grid is tiles x splits, part p of a tile taking
+  // its chunks [p T_all / splits, (p + 1) T_all / splits) (the plan keeps splits <= T_all).
+  const int tiles = static_cast<int>(gridDim.x) / splits;
+  const int tile = static_cast<int>(blockIdx.x) % tiles;
+  const int part = static_cast<int>(blockIdx.x) / tiles;
   int mi = 0;
   if constexpr (NP > 1)
     while (mi + 1 < parts.count && tile >= parts.gbeg[mi + 1]) ++mi;
@@ -128,10 +135,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   const uint8_t* const wrow =
       (NP > 1 ? parts.w[mi] : parts.w[0]) + static_cast<int64_t>(min(r0 + col, n_part - 1)) * rowbytes;
 
-  // Chunk t covers units G t .. G t + G - 1 of every row: lane group g takes unit
-  // G t + g. Past the row end the address is clamped and the weights are zeroed.
-  const int T = (nu + G - 1) / G;
-  auto unit_ptr = [&](int t) { return wrow + static_cast<int64_t>(min(G * t + g, nu - 1)) * UB; };
+  // Chunk c covers units G c .. G c + G - 1 of every row: lane group g takes unit
+  // G c + g (past the row end the address is clamped). This part's chunks are
+  // c = t_off + t, t < T.
+  const int T_all = (nu + G - 1) / G;
+  const int t_off = part * T_all / splits;
+  const int T = (part + 1) * T_all / splits - t_off;
+  auto unit_ptr = [&](int t) { return wrow + static_cast<int64_t>(min(G * (t_off + t) + g, nu - 1)) * UB; };
 
   // Decode table (threads 0..127).
   if (threadIdx.x < 128) {
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
       const int p = i % PU;
       const int bu = i / PU;
       const int b = bu / G;
-      const int unit = G * t + (bu % G);
+      const int unit = G * (t_off + t) + (bu % G);
       const uint4 v = *reinterpret_cast<const uint4*>(x + b * ldx + 32 * P * min(unit, nu - 1) + 8 * p);
       c.v[j] = unit < nu ? v : uint4{0u, 0u, 0u, 0u};
     }
@@ -269,6 +279,42 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     acc[3] += o[3];
   }
   const int row = r0 + col;
+  if (splits > 1) {
+    // Leave this part's sums (tile-major, weight row, batch row), then let the last part
+    // to arrive add all parts in part order, so the result does not depend on the
+    // arrival order. The sums and counters are written and read with agent-scope
+    // accesses (coherent across the XCDs' L2 caches without flushing them, as full
+    // release/acquire fences would, which measured 3-5x slower), and the sums are
+    // complete (s_waitcnt) before the arrival is counted.
+    float* const mine = partial + (static_cast<int64_t>(part) * tiles + tile) * 128;
+    if (lane < 32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(&mine[col * 8 + 4 * (lane >> 4) + i], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int prior = 0;
+    if (lane == 0) prior = __hip_atomic_fetch_add(&arrivals[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__shfl(prior, 0, 64) != splits - 1) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane < 32 && row < n_part) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 4 * (lane >> 4) + i;
+        if (b < batch) {
+          float sum = 0.f;
+          for (int q = 0; q < splits; ++q)
+            sum += __hip_atomic_load(&partial[(static_cast<int64_t>(q) * tiles + tile) * 128 + col * 8 + b],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          y[b * ldy + row] = sum;
+        }
+      }
+    }
+    if (lane == 0) __hip_atomic_store(&arrivals[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   if (row < n_part) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -279,10 +325,32 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
 }
 
 struct MfmaPlan {
-  int p, nu, tiles;
+  int p, nu, tiles, splits;
   bool big;
   size_t shm;
 };
+
+// Split chunks: launches of long rows and few tiles give each tile's chunks to two
+// workgroups, so that every CU gets work. Measured (same box, us): 5120 x 17408 (17
+// chunks per row, 320 tiles) batch 2/4/8 22.3/23.8/34.1 unsplit, 20.2/21.9/28.4 in two
+// parts, 21.2/23.4/32.3 in four; rows of 5-6 chunks (6144 x 5120, 5120 x 6144, 1024 x
+// 5120) are slower split, since combining the parts adds round trips to memory at the
+// end of a short launch. The partial sums and arrival counters live in a
+// per-(device, stream) workspace: the counters first (a fixed region for up to
+// kMaxSplitTiles tiles, zero at allocation and reset by each launch), then the sums.
+// RFP4_GEMV_SPLIT = "1", "2" or "4", read on each call, forces a split (reduced to at
+// least one chunk per part).
+constexpr int kMaxSplitTiles = 1024;
+constexpr size_t kSplitCounterBytes = kMaxSplitTiles * sizeof(int);
+inline int mfma_splits(int tiles, int nu) {
+  const int t_all = (nu + 4 * kMfmaWaves - 1) / (4 * kMfmaWaves);
+  int s = (tiles < 4 * device_cu_count() && t_all >= 12) ? 2 : 1;
+  const char* env = getenv("RFP4_GEMV_SPLIT");
+  if (env != nullptr && (env[0] == '1' || env[0] == '2' || env[0] == '4') && env[1] == '\0') s = env[0] - '0';
+  if (tiles > kMaxSplitTiles) s = 1;
+  while (s > 1 && t_all < s) s /= 2;
+  return s;
+}
 
 // LDS of a launch: the table plus one activation chunk (or the cross-wavefront sums,
 // if larger).
@@ -300,21 +368,36 @@ inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch) {
   for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 15) / 16);
   pl.big = batch > 4;
   pl.shm = mfma_lds(pl.p, batch);
+  pl.splits = mfma_splits(pl.tiles, pl.nu);
   return pl;
 }
 
 template <int LAYOUT, int XT, int P, bool BIG, int NP>
 hipError_t launch_mfma_p(const MfmaPlan& pl, const GemvParts<NP>& gp, const uint16_t* x, int64_t ldx,
-                         int batch, hipStream_t stream) {
-  gemv_mfma_kernel<LAYOUT, XT, P, BIG, NP><<<dim3(pl.tiles), dim3(64 * kMfmaWaves), pl.shm, stream>>>(
-      gp, pl.nu, x, ldx, batch);
+                         int batch, float* partial, int* arrivals, hipStream_t stream) {
+  gemv_mfma_kernel<LAYOUT, XT, P, BIG, NP>
+      <<<dim3(static_cast<unsigned>(pl.tiles) * pl.splits), dim3(64 * kMfmaWaves), pl.shm, stream>>>(
+          gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals);
   return hipGetLastError();
 }
 
 template <int LAYOUT, int XT, int NP>
 hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t* x, int batch,
                        int64_t ldx, hipStream_t stream) {
-  const MfmaPlan pl = mfma_plan(parts, count, nb, batch);
+  MfmaPlan pl = mfma_plan(parts, count, nb, batch);
+  float* partial = nullptr;
+  int* arrivals = nullptr;
+  if (pl.splits > 1) {
+    const size_t bytes = kSplitCounterBytes + static_cast<size_t>(pl.splits) * pl.tiles * 128 * sizeof(float);
+    void* ws = nullptr;
+    if (stream_workspace(kWorkspaceGemv, stream, bytes, &ws) != hipSuccess) {
+      (void)hipGetLastError();  // no workspace (first call under graph capture): no split
+      pl.splits = 1;
+    } else {
+      arrivals = static_cast<int*>(ws);
+      partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCounterBytes);
+    }
+  }
   GemvParts<NP> gp;
   gp.count = count;
   gp.gbeg[0] = 0;
@@ -326,10 +409,10 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
     gp.gbeg[i + 1] = gp.gbeg[i] + static_cast<int>((parts[i].n + 15) / 16);
   }
   if (pl.p == 2)
-    return pl.big ? launch_mfma_p<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, stream)
-                  : launch_mfma_p<LAYOUT, XT, 2, false, NP>(pl, gp, x, ldx, batch, stream);
-  return pl.big ? launch_mfma_p<LAYOUT, XT, 1, true, NP>(pl, gp, x, ldx, batch, stream)
-                : launch_mfma_p<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, stream);
+    return pl.big ? launch_mfma_p<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream)
+                  : launch_mfma_p<LAYOUT, XT, 2, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream);
+  return pl.big ? launch_mfma_p<LAYOUT, XT, 1, true, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream)
+                : launch_mfma_p<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream);
 }
 
 // Matrix-core path for the batches where it is faster: measured on the decode shapes,

@@ -21,6 +21,13 @@ constexpr int block_bytes(int layout) { return layout == kDual ? 18 : 17; }
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Per-(kind, device, stream) device workspace of at least `bytes`, zero-filled when
+// (re)allocated, kept until the process ends; hipErrorStreamCaptureUnsupported while
+// the stream is being captured and the workspace is too small.
+constexpr int kWorkspaceGemm = 0;  // k-split partial tiles of rfp4_gemm
+constexpr int kWorkspaceGemv = 1;  // split-chunk partial sums and arrival counters of rfp4_gemv
+hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void** out);
+
 // Launchers. Arguments have been checked by the API layer: shapes in range, rows
 // 16-byte aligned, pointers non-null and aligned as the public header requires.
 hipError_t launch_dequant(const uint8_t* w, int layout, int64_t n, int64_t k, float* out,

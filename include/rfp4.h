@@ -23,11 +23,12 @@
  *
  * General rules for every entry point:
  *   - All pointers except rfp4_validate's `w_host` are device pointers. The caller
- *     owns every buffer it passes. The dequant and GEMV entry points never
- *     allocate, free or synchronize; rfp4_gemm may use a workspace of its own and
- *     rfp4_gemm_dequant uses rocBLAS (see there). Global state: per-device caches of
- *     the CU count and of kernel attributes (atomics), rfp4_gemm's workspaces and
- *     the rocBLAS handles (behind mutexes), so calls from several threads are safe.
+ *     owns every buffer it passes. The dequant and encoder entry points never
+ *     allocate, free or synchronize; rfp4_gemm and rfp4_gemv(_multi) may use a
+ *     workspace of their own (see there) and rfp4_gemm_dequant uses rocBLAS. Global
+ *     state: per-device caches of the CU count and of kernel attributes (atomics),
+ *     the workspaces and the rocBLAS handles (behind mutexes), so calls from several
+ *     threads are safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are
  *     asynchronous and ordered on that stream; a fault in a kernel surfaces at the
  *     caller's next synchronization.
@@ -117,7 +118,16 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n. Batch 1 runs a
  * dot-product kernel, batches from 2 on a matrix-core kernel (the summation order,
  * hence the last bits, differ between the two); the environment variable
- * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. */
+ * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. On long rows
+ * (at least 12 chunks of 16 units, a unit being two blocks when k / 32 is even and one
+ * otherwise: k >= 11328 or k >= 5664) with fewer than four 16-row tiles per CU the
+ * matrix-core kernel gives
+ * each tile's k range to two workgroups whose fp32 partial sums meet in a small
+ * device workspace (under 1 MB) that the library allocates per (device, stream) on
+ * first need and keeps; the parts are added in a fixed order, so results are
+ * deterministic. It is never allocated during graph capture (the launch then runs
+ * unsplit, which changes the last bits), so call once before capturing.
+ * RFP4_GEMV_SPLIT = "1", "2" or "4" forces the number of parts. */
 RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const void* x,
                       int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,
                       void* stream);

@@ -828,6 +828,65 @@ def test_gemv_mfma_multi(case, monkeypatch):
         assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
 
 
+SPLIT_CASES = [  # layout, n, k, batch, dtype, forced split (reduced to one chunk per part)
+    (1, 5120, 17408, 8, "bf16", 2), (1, 5120, 17408, 2, "bf16", 4), (0, 1024, 5120, 3, "f16", 4),
+    (0, 33, 1408, 4, "f16", 2), (0, 1, 256, 5, "f16", 4), (1, 45, 1056, 6, "bf16", 4),
+    (0, 300, 4000, 8, "bf16", 4), (0, 999, 2304, 7, "f16", 2), (1, 5120, 6144, 4, "bf16", 1),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "L{}n{}k{}b{}{}-s{}".format(*c))
+def test_gemv_mfma_split(case, monkeypatch):
+    """Each tile's chunks shared by 1, 2 or 4 workgroups whose partial sums meet in the
+    stream's workspace; padded output rows stay untouched."""
+    layout, n, k, batch, dt, split = case
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    monkeypatch.setenv("RFP4_GEMV_SPLIT", str(split))
+    rng = np.random.default_rng(9400 + n + k + batch)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    x = synth.activations(rng, batch, k, dt)
+    check_gemv(w, layout, n, k, x, ldy=n + 5)
+
+
+def test_gemv_mfma_split_launch_sequence(monkeypatch):
+    """Launches with different splits and tile counts back to back on one stream (the
+    arrival counters must be back at zero after each), then the first one again."""
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    rng = np.random.default_rng(9450)
+    shapes = [(0, 700, 2048, 4, 4), (1, 130, 6144, 8, 2), (0, 700, 2048, 4, 2), (0, 64, 5120, 2, 4),
+              (0, 700, 2048, 4, 4)]
+    data = {}
+    for layout, n, k, batch, _ in shapes:
+        if (layout, n, k, batch) not in data:
+            w = synth.weights(rng, layout, n, k)
+            x = synth.activations(rng, batch, k, "f16")
+            y_ref, den = O.gemv(w, layout, n, k, x64(x))
+            data[(layout, n, k, batch)] = (dev(w), x.to(DEV).contiguous(), y_ref, den)
+    ys = []
+    for layout, n, k, batch, split in shapes:
+        monkeypatch.setenv("RFP4_GEMV_SPLIT", str(split))
+        wd, xd, _, _ = data[(layout, n, k, batch)]
+        ys.append(R.rfp4_gemv(wd, layout, n, k, xd))
+    torch.cuda.synchronize()
+    for (layout, n, k, batch, _), y in zip(shapes, ys):
+        _, _, y_ref, den = data[(layout, n, k, batch)]
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
+
+
+def test_gemv_mfma_multi_split(monkeypatch):
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    monkeypatch.setenv("RFP4_GEMV_SPLIT", "4")
+    layout, ns, k, batch = 1, [300, 45, 1000, 7], 6144, 5
+    rng = np.random.default_rng(9460)
+    ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
+    x = synth.activations(rng, batch, k, "bf16")
+    ys = R.rfp4_gemv_multi([dev(w) for w in ws], layout, ns, k, x.to(DEV).contiguous())
+    torch.cuda.synchronize()
+    for w, n, y in zip(ws, ns, ys):
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
+
+
 def test_gemv_mfma_zero_scales_give_zero(monkeypatch):
     monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
     layout, n, k, batch = 0, 40, 512, 4
@@ -841,10 +900,11 @@ def test_gemv_mfma_zero_scales_give_zero(monkeypatch):
 # ------------------------------------------------------------------ graph capture
 
 def test_graph_replay_matches_eager(monkeypatch):
-    """Every entry point captured into one HIP graph (batch-1 and batch-4 GEMV, a GEMM
-    with split k, dequant, encoder) and replayed three times, with eager work between
-    the replays, gives exactly the eager results. The GEMM runs eagerly first so that
-    its workspace exists before the capture, as the header asks."""
+    """Every entry point captured into one HIP graph (batch-1 and batch-4 GEMV, a
+    batch-4 GEMV on long rows whose tiles split, a GEMM with split k, dequant, encoder)
+    and replayed three times, with eager work between the replays, gives exactly the
+    eager results. Everything runs on the capture stream first so that the workspaces
+    exist before the capture, as the header asks."""
     monkeypatch.setenv("RFP4_GEMM_PLAN", "tail2")
     rng = np.random.default_rng(9500)
     layout, n, k = 0, 1040, 2048
@@ -854,13 +914,18 @@ def test_graph_replay_matches_eager(monkeypatch):
     a = synth.activations(rng, 200, k, "bf16").to(DEV).contiguous()
     src = synth.real_weights(rng, 96, k, "bf16").to(DEV).contiguous()
 
-    outs = {"y1": torch.empty((1, n), dtype=torch.float32, device=DEV),
+    ws_layout, ws_n, ws_k = 1, 520, 12288  # long rows: the batch-4 GEMV splits its tiles
+    wsd = dev(synth.weights(rng, ws_layout, ws_n, ws_k))
+    xs4 = synth.activations(rng, 4, ws_k, "bf16").to(DEV).contiguous()
+    outs = {"ys": torch.empty((4, ws_n), dtype=torch.float32, device=DEV),
+            "y1": torch.empty((1, n), dtype=torch.float32, device=DEV),
             "y4": torch.empty((4, n), dtype=torch.float32, device=DEV),
             "c": torch.empty((200, n), dtype=torch.bfloat16, device=DEV),
             "d": torch.empty((n, k), dtype=torch.float32, device=DEV),
             "q": torch.empty((96, R.rfp4_row_bytes(layout, k)), dtype=torch.uint8, device=DEV)}
 
     def run():
+        R.rfp4_gemv(wsd, ws_layout, ws_n, ws_k, xs4, y=outs["ys"])
         R.rfp4_gemv(wd, layout, n, k, x1, y=outs["y1"])
         R.rfp4_gemv(wd, layout, n, k, x4, y=outs["y4"])
         R.rfp4_gemm(wd, layout, n, k, a, c=outs["c"])
