@@ -1,5 +1,5 @@
 // Fused dequant + GEMV for decode: y[b][r] = sum_c W[r][c] * x[b][c], batch 1..8 (the
-// dot-product kernel; batches from 3 on default to the matrix-core kernel of
+// dot-product kernel; batches from 2 on default to the matrix-core kernel of
 // gemv_mfma.h).
 //
 // The page names gemv as the decode hot path ("Feasibility Report: Porting ROCmFP4
