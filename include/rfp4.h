@@ -126,7 +126,9 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * device workspace (under 1 MB) that the library allocates per (device, stream) on
  * first need and keeps; the parts are added in a fixed order, so results are
  * deterministic. It is never allocated during graph capture (the launch then runs
- * unsplit, which changes the last bits), so call once before capturing.
+ * unsplit, which changes the last bits), so call once before capturing. A captured
+ * split launch keeps using the capturing stream's workspace: replay such a graph only
+ * ordered with that stream's other work and with its own other replays.
  * RFP4_GEMV_SPLIT = "1", "2" or "4" forces the number of parts. */
 RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const void* x,
                       int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,
@@ -163,7 +165,9 @@ RFP4_API rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int6
  * needed (synchronizing that stream first) and keeps until the process ends; a
  * final kernel adds the parts in a fixed order and rounds to bf16. The workspace is
  * never allocated while the stream is being captured into a graph (the split is
- * then skipped), so call once before capturing. Results are deterministic for a
+ * then skipped), so call once before capturing; a captured split launch keeps using
+ * the capturing stream's workspace, so replay such a graph only ordered with that
+ * stream's other work and with its own other replays. Results are deterministic for a
  * given shape and CU count. The environment variable RFP4_GEMM_PLAN, read on each
  * call, forces a plan: "main" (256 x 256 tiles only), "msplit2", "msplit3", "msplit4"
  * (256 x 256 tiles only, k split 2, 3 or 4 ways), "tail", "tail2", "tail4" (128 x 128
