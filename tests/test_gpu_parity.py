@@ -978,3 +978,19 @@ def test_gemv_split_two_streams(monkeypatch):
         for rep in range(6):
             assert O.normalized_error(ys[s][rep].cpu().numpy(), y_ref, den) <= TOL
             assert torch.equal(ys[s][rep], ys[s][0])
+
+
+@pytest.mark.parametrize("mode,batch", [("0", 1), ("1", 4)])
+def test_gemv_vocab_rows_sampled(mode, batch, monkeypatch):
+    """A vocabulary-sized matrix (152064 x 5120 dual, 438 MB packed: the decode LM head)
+    on either kernel, checked on a seeded sample of rows that includes the first and the
+    last."""
+    monkeypatch.setenv("RFP4_GEMV_MFMA", mode)
+    layout, n, k = 0, 152064, 5120
+    rng = np.random.default_rng(9700 + batch)
+    w = synth.weights(rng, layout, n, k)
+    x = synth.activations(rng, batch, k, "f16")
+    y = R.rfp4_gemv(dev(w), layout, n, k, x.to(DEV).contiguous()).cpu().numpy()
+    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], rng.choice(n, 96, replace=False)]))
+    y_ref, den = O.gemv_rows(w, layout, n, k, x64(x), rows)
+    assert O.normalized_error(y[:, rows], y_ref, den) <= TOL
