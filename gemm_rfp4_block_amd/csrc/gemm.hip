@@ -934,8 +934,7 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
       float* ws = nullptr;
       if (stream_workspace(kWorkspaceGemm, stream, main_bytes + tail_bytes, reinterpret_cast<void**>(&ws)) !=
           hipSuccess) {
-        (void)hipGetLastError();  // clear a failed allocation; run every tile unsplit
-        plan.splits = 1;
+        plan.splits = 1;  // no workspace (graph capture or no memory): run every tile unsplit
         plan.main_splits = 1;
       } else {
         partial_main = ws;

@@ -49,6 +49,7 @@ hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void** o
     }
     e = hipMalloc(&en->ptr, bytes);
     if (e != hipSuccess) {
+      (void)hipGetLastError();  // the failed allocation's error is reported here, not later
       en->ptr = nullptr;
       return e;
     }

@@ -391,8 +391,7 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
     const size_t bytes = kSplitCounterBytes + static_cast<size_t>(pl.splits) * pl.tiles * 128 * sizeof(float);
     void* ws = nullptr;
     if (stream_workspace(kWorkspaceGemv, stream, bytes, &ws) != hipSuccess) {
-      (void)hipGetLastError();  // no workspace (first call under graph capture): no split
-      pl.splits = 1;
+      pl.splits = 1;  // no workspace (first call under graph capture, or no memory): no split
     } else {
       arrivals = static_cast<int*>(ws);
       partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCounterBytes);
