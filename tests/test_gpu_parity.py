@@ -483,6 +483,21 @@ def test_gemm_split_main_tiles_full_size_sampled(monkeypatch):
     assert gemm_error(c[:, cols], c_ref, den) <= TOL
 
 
+def test_gemm_large_ragged_m_sampled():
+    """3000 token rows (not a multiple of the 256-row tile) against the 17408 x 5120
+    up-projection: more than four rounds of main tiles plus the planner's tail; sampled
+    columns, every row, including the last partial row tile."""
+    layout, m, n, k = 0, 3000, 17408, 5120
+    w = synth.weights(np.random.default_rng(4500), layout, n, k)
+    a = synth.activations(np.random.default_rng(4501), m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a)
+    edges = np.array([0, 255, 256, n - 1025, n - 1024, n - 257, n - 256, n - 1])
+    cols = np.unique(np.concatenate([np.random.default_rng(4502).choice(n, 40, replace=False), edges]))
+    c_ref, den = O.gemm_rows(w, layout, n, k, x64(a), cols)
+    assert gemm_error(c[:, cols], c_ref, den) <= TOL
+    assert np.all(np.isfinite(c))
+
+
 def test_gemm_mixed_tile_sizes():
     """2048 x 8448: 256 full tiles plus one strip of 256 columns that the launcher computes
     as 128 x 128 tiles with the k range split in two (partial sums, then a reduction);
