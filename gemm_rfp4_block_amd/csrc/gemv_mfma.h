@@ -4,7 +4,9 @@
 //   y[b][r] = sum_c weight(r, c) * x[b][c]
 //
 // Mapping. A workgroup of four wavefronts (one per SIMD) owns 16 consecutive weight
-// rows (one MFMA tile of v_mfma_f32_16x16x32_{f16,bf16}). Lane l of a wavefront serves
+// rows (one MFMA tile of v_mfma_f32_16x16x32_{f16,bf16}), or R = 2 such tiles (32 rows,
+// two accumulators per wavefront sharing each activation fragment) for batches above 4
+// on large launches. Lane l of a wavefront serves
 // as B-operand lane for weight row l % 16 and as A-operand lane for activation row
 // l % 16 (rows beyond the batch read a clamped, finite row whose results are never
 // stored); the lane group g = 4 w + l / 16 (w the wavefront) takes units g, g + 16,
@@ -98,7 +100,7 @@ __device__ __forceinline__ void unit_scale_bytes(const UnitRaw<P>& u, uint32_t& 
 
 constexpr int kMfmaWaves = 4;
 
-template <int LAYOUT, int XT, int P, bool BIG, int NP>
+template <int LAYOUT, int XT, int P, bool BIG, int R, int NP>
 __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvParts<NP> parts, int nu,
                                                            const uint16_t* __restrict__ x,
                                                            int64_t ldx, int batch, int splits,
@@ -110,6 +112,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   constexpr int G = 4 * W;        // lane groups: units of a row per chunk
   constexpr int PU = 4 * P;       // 16-byte activation pieces per unit
   constexpr int XPT = BIG ? 2 * P : P;  // pieces per thread per chunk: batch <= 8 or <= 4
+  constexpr int D = R == 2 ? 2 : 3;     // chunks in flight (two with two tiles: registers)
   typedef MfmaOps<XT> M;
   extern __shared__ uint4 smem_m[];
 
@@ -130,10 +133,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   if constexpr (NP > 1)
     while (mi + 1 < parts.count && tile >= parts.gbeg[mi + 1]) ++mi;
   const int n_part = NP > 1 ? parts.n[mi] : parts.n[0];
-  const int r0 = (tile - (NP > 1 ? parts.gbeg[mi] : 0)) * 16;
+  const int r0 = (tile - (NP > 1 ? parts.gbeg[mi] : 0)) * 16 * R;
   const int64_t rowbytes = static_cast<int64_t>(nu) * UB;
-  const uint8_t* const wrow =
-      (NP > 1 ? parts.w[mi] : parts.w[0]) + static_cast<int64_t>(min(r0 + col, n_part - 1)) * rowbytes;
+  const uint8_t* wrow[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+    wrow[q] = (NP > 1 ? parts.w[mi] : parts.w[0]) + static_cast<int64_t>(min(r0 + 16 * q + col, n_part - 1)) * rowbytes;
 
   // Chunk c covers units G c .. G c + G - 1 of every row: lane group g takes unit
   // G c + g (past the row end the address is clamped). This part's chunks are
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   const int T_all = (nu + G - 1) / G;
   const int t_off = part * T_all / splits;
   const int T = (part + 1) * T_all / splits - t_off;
-  auto unit_ptr = [&](int t) { return wrow + static_cast<int64_t>(min(G * (t_off + t) + g, nu - 1)) * UB; };
+  auto unit_ptr = [&](int q, int t) { return wrow[q] + static_cast<int64_t>(min(G * (t_off + t) + g, nu - 1)) * UB; };
 
   // Decode table (threads 0..127).
   if (threadIdx.x < 128) {
@@ -192,42 +197,53 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   // Three chunks in flight: the activations of chunk t are loaded just before its
   // weights, so the LDS store of chunk t waits for exactly those loads and leaves the
   // weights of chunk t (and later) in flight.
-  XChunk xr[3];
-  UnitRaw<P> rb[3];
+  XChunk xr[D];
+  UnitRaw<P> rb[R][D];
 #pragma unroll
-  for (int d = 0; d < 3; ++d) {
+  for (int d = 0; d < D; ++d) {
     const int tc = min(d, T - 1);  // straight-line loads; a chunk past T is never used
     xr[d] = x_load(tc);
-    load_unit<LAYOUT, P>(unit_ptr(tc), rb[d]);
+#pragma unroll
+    for (int q = 0; q < R; ++q) load_unit<LAYOUT, P>(unit_ptr(q, tc), rb[q][d]);
   }
 
   const int xb = min(col, batch - 1);  // activation row of this A lane (clamped)
-  mf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mf32x4 acc[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) acc[q] = mf32x4{0.f, 0.f, 0.f, 0.f};
 
   // A lane group past the row end holds the row's last unit of weights against zeroed
   // activations, so it adds zeros.
-  auto consume = [&](const UnitRaw<P>& u) {
+  auto consume = [&](int d) {
     const uint4* const xu = xs + (xb * G + g) * (PU + 1);
     auto block = [&](auto b_c) {
       constexpr int B = decltype(b_c)::value;
-      const uint4 q = unit_qs<LAYOUT, P, B>(u);
-      uint32_t e0, e1;
-      unit_scale_bytes<LAYOUT, P, B>(u, e0, e1);
-      const uint4 t0 = lut[e0];
-      const uint4 t1 = LAYOUT == kDual ? lut[e1] : t0;
-      const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+      uint4 q4[R], t0[R], t1[R];
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        q4[q] = unit_qs<LAYOUT, P, B>(rb[q][d]);
+        uint32_t e0, e1;
+        unit_scale_bytes<LAYOUT, P, B>(rb[q][d], e0, e1);
+        t0[q] = lut[e0];
+        t1[q] = LAYOUT == kDual ? lut[e1] : t0[q];
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t qa = qw[2 * (s & 1)], qb = qw[2 * (s & 1) + 1];
-        uint2 pa, pb;
-        if (s < 2) {  // low nibbles: first half (scale e0)
-          pa = decode_plane(qa & 0x07070707u, (qa << 4) & 0x80808080u, t0);
-          pb = decode_plane(qb & 0x07070707u, (qb << 4) & 0x80808080u, t0);
-        } else {  // high nibbles: second half (scale e1)
-          pa = decode_plane((qa >> 4) & 0x07070707u, qa & 0x80808080u, t1);
-          pb = decode_plane((qb >> 4) & 0x07070707u, qb & 0x80808080u, t1);
+        const uint4 a = xu[4 * B + s];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          const uint32_t qw[4] = {q4[q].x, q4[q].y, q4[q].z, q4[q].w};
+          const uint32_t qa = qw[2 * (s & 1)], qb = qw[2 * (s & 1) + 1];
+          uint2 pa, pb;
+          if (s < 2) {  // low nibbles: first half (scale e0)
+            pa = decode_plane(qa & 0x07070707u, (qa << 4) & 0x80808080u, t0[q]);
+            pb = decode_plane(qb & 0x07070707u, (qb << 4) & 0x80808080u, t0[q]);
+          } else {  // high nibbles: second half (scale e1)
+            pa = decode_plane((qa >> 4) & 0x07070707u, qa & 0x80808080u, t1[q]);
+            pb = decode_plane((qb >> 4) & 0x07070707u, qb & 0x80808080u, t1[q]);
+          }
+          acc[q] = M::mfma(a, uint4{pa.x, pa.y, pb.x, pb.y}, acc[q]);
         }
-        acc = M::mfma(xu[4 * B + s], uint4{pa.x, pa.y, pb.x, pb.y}, acc);
       }
     };
     block(std::integral_constant<int, 0>{});
@@ -242,25 +258,26 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   // nothing and skips the chunks past T, so no load outlives the last multiply. The
   // first barrier also orders the table writes before their first reads.
   int t = 0;
-  for (; t + 3 < T; t += 3) {
+  for (; t + D < T; t += D) {
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
+    for (int d = 0; d < D; ++d) {
       if (t + d > 0) __syncthreads();
       x_store(xr[d]);
       __syncthreads();
-      consume(rb[d]);
-      const int tn = min(t + d + 3, T - 1);
+      consume(d);
+      const int tn = min(t + d + D, T - 1);
       xr[d] = x_load(tn);
-      load_unit<LAYOUT, P>(unit_ptr(tn), rb[d]);
+#pragma unroll
+      for (int q = 0; q < R; ++q) load_unit<LAYOUT, P>(unit_ptr(q, tn), rb[q][d]);
     }
   }
 #pragma unroll
-  for (int d = 0; d < 3; ++d) {
+  for (int d = 0; d < D; ++d) {
     if (t + d < T) {
       if (t + d > 0) __syncthreads();
       x_store(xr[d]);
       __syncthreads();
-      consume(rb[d]);
+      consume(d);
     }
   }
 
@@ -268,18 +285,22 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   float* const y = NP > 1 ? parts.y[mi] : parts.y[0];
   const int64_t ldy = NP > 1 ? parts.ldy[mi] : parts.ldy[0];
   __syncthreads();  // the last chunk's reads are done before its LDS is reused
-  red[wv * 64 + lane] = acc;
+#pragma unroll
+  for (int q = 0; q < R; ++q) red[(q * W + wv) * 64 + lane] = acc[q];
   __syncthreads();
   if (wv != 0) return;
-  for (int w = 1; w < W; ++w) {
-    const mf32x4 o = red[w * 64 + lane];
-    acc[0] += o[0];
-    acc[1] += o[1];
-    acc[2] += o[2];
-    acc[3] += o[3];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    for (int w = 1; w < W; ++w) {
+      const mf32x4 o = red[(q * W + w) * 64 + lane];
+      acc[q][0] += o[0];
+      acc[q][1] += o[1];
+      acc[q][2] += o[2];
+      acc[q][3] += o[3];
+    }
   }
   const int row = r0 + col;
-  if (splits > 1) {
+  if (R == 1 && splits > 1) {
     // Leave this part's sums (tile-major, weight row, batch row), then let the last part
     // to arrive add all parts in part order, so the result does not depend on the
     // arrival order. The sums and counters are written and read with agent-scope
@@ -290,7 +311,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     if (lane < 32) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(&mine[col * 8 + 4 * (lane >> 4) + i], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&mine[col * 8 + 4 * (lane >> 4) + i], acc[0][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
@@ -315,17 +336,20 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     if (lane == 0) __hip_atomic_store(&arrivals[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (row < n_part) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * (lane >> 4) + i;
-      if (b < batch) y[b * ldy + row] = acc[i];
+  for (int q = 0; q < R; ++q) {
+    if (row + 16 * q < n_part) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 4 * (lane >> 4) + i;
+        if (b < batch) y[b * ldy + row + 16 * q] = acc[q][i];
+      }
     }
   }
 }
 
 struct MfmaPlan {
-  int p, nu, tiles, splits;
+  int p, nu, tiles, splits, r;
   bool big;
   size_t shm;
 };
@@ -354,9 +378,9 @@ inline int mfma_splits(int tiles, int nu) {
 
 // LDS of a launch: the table plus one activation chunk (or the cross-wavefront sums,
 // if larger).
-inline size_t mfma_lds(int p, int batch) {
+inline size_t mfma_lds(int p, int batch, int r) {
   const size_t chunk = static_cast<size_t>(batch) * 4 * kMfmaWaves * (4 * p + 1) * 16;
-  const size_t red = static_cast<size_t>(kMfmaWaves) * 64 * 16;
+  const size_t red = static_cast<size_t>(r) * kMfmaWaves * 64 * 16;
   return 128 * 16 + (chunk > red ? chunk : red);
 }
 
@@ -364,20 +388,31 @@ inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch) {
   MfmaPlan pl;
   pl.p = nb % 2 == 0 ? 2 : 1;
   pl.nu = nb / pl.p;
-  pl.tiles = 0;
-  for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 15) / 16);
+  int tiles16 = 0;
+  for (int i = 0; i < count; ++i) tiles16 += static_cast<int>((parts[i].n + 15) / 16);
   pl.big = batch > 4;
-  pl.shm = mfma_lds(pl.p, batch);
-  pl.splits = mfma_splits(pl.tiles, pl.nu);
+  // Two tiles per workgroup (sharing each staged activation chunk) for batches above 4
+  // on launches of many tiles: 152064 x 5120 batch 5/8 145.8/156.1 -> 120.0/127.9 us,
+  // 17408 x 5120 batch 8 24.2 -> 23.6 us; at batches <= 4 it was slower on 17408 x 5120
+  // (16.7 -> 19.4 us at batch 2).
+  pl.r = (pl.big && tiles16 >= 4 * device_cu_count()) ? 2 : 1;
+  pl.tiles = 0;
+  for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 16 * pl.r - 1) / (16 * pl.r));
+  pl.shm = mfma_lds(pl.p, batch, pl.r);
+  pl.splits = pl.r == 1 ? mfma_splits(pl.tiles, pl.nu) : 1;
   return pl;
 }
 
 template <int LAYOUT, int XT, int P, bool BIG, int NP>
 hipError_t launch_mfma_p(const MfmaPlan& pl, const GemvParts<NP>& gp, const uint16_t* x, int64_t ldx,
                          int batch, float* partial, int* arrivals, hipStream_t stream) {
-  gemv_mfma_kernel<LAYOUT, XT, P, BIG, NP>
-      <<<dim3(static_cast<unsigned>(pl.tiles) * pl.splits), dim3(64 * kMfmaWaves), pl.shm, stream>>>(
-          gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals);
+  const dim3 grid(static_cast<unsigned>(pl.tiles) * pl.splits), block(64 * kMfmaWaves);
+  if (BIG && pl.r == 2)
+    gemv_mfma_kernel<LAYOUT, XT, P, BIG, BIG ? 2 : 1, NP><<<grid, block, pl.shm, stream>>>(
+        gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals);
+  else
+    gemv_mfma_kernel<LAYOUT, XT, P, BIG, 1, NP><<<grid, block, pl.shm, stream>>>(
+        gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals);
   return hipGetLastError();
 }
 
@@ -405,7 +440,7 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
     gp.y[i] = parts[i].y;
     gp.ldy[i] = parts[i].ldy;
     gp.n[i] = static_cast<int>(parts[i].n);
-    gp.gbeg[i + 1] = gp.gbeg[i] + static_cast<int>((parts[i].n + 15) / 16);
+    gp.gbeg[i + 1] = gp.gbeg[i] + static_cast<int>((parts[i].n + 16 * pl.r - 1) / (16 * pl.r));
   }
   if (pl.p == 2)
     return pl.big ? launch_mfma_p<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream)

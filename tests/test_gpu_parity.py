@@ -799,6 +799,9 @@ MFMA_CASES = [  # layout, n, k, batch, dtype
     # single-block units and a ragged last chunk, 6 exactly at batch 4
     (0, 200, 4096, 4, "f16"), (1, 77, 6912, 5, "bf16"), (0, 50, 2720, 6, "bf16"),
     (1, 5120, 6144, 4, "bf16"),
+    # two tiles per workgroup (batch > 4, >= 1024 tiles): n % 32 == 16 leaves the last
+    # workgroup's second tile empty; single-block units
+    (0, 16400, 512, 6, "f16"), (1, 16400, 1056, 8, "bf16"),
 ]
 
 
@@ -885,6 +888,21 @@ def test_gemv_mfma_split_launch_sequence(monkeypatch):
     torch.cuda.synchronize()
     for (layout, n, k, batch, _), y in zip(shapes, ys):
         _, _, y_ref, den = data[(layout, n, k, batch)]
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
+
+
+def test_gemv_mfma_multi_two_tiles(monkeypatch):
+    """Two matrices fused at batch 7 with enough tiles for two tiles per workgroup: the
+    32-row tiles of each part start at the part's first row."""
+    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    layout, ns, k, batch = 0, [9000, 8008], 256, 7
+    rng = np.random.default_rng(9470)
+    ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
+    x = synth.activations(rng, batch, k, "f16")
+    ys = R.rfp4_gemv_multi([dev(w) for w in ws], layout, ns, k, x.to(DEV).contiguous())
+    torch.cuda.synchronize()
+    for w, n, y in zip(ws, ns, ys):
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
         assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
 
 
@@ -995,7 +1013,7 @@ def test_gemv_split_two_streams(monkeypatch):
             assert torch.equal(ys[s][rep], ys[s][0])
 
 
-@pytest.mark.parametrize("mode,batch", [("0", 1), ("1", 4)])
+@pytest.mark.parametrize("mode,batch", [("0", 1), ("1", 4), ("1", 8)])
 def test_gemv_vocab_rows_sampled(mode, batch, monkeypatch):
     """A vocabulary-sized matrix (152064 x 5120 dual, 438 MB packed: the decode LM head)
     on either kernel, checked on a seeded sample of rows that includes the first and the
