@@ -242,7 +242,7 @@ __device__ __forceinline__ void unit_scales(const UnitRaw<P>& u, float& s0, floa
 
 // One block: decode 32 weights and accumulate them against every activation row.
 // `xunit(b, cc)` returns the 16-byte activation unit cc (values 8cc..8cc+7 of the
-// block) of activation row b. Each half's dot product is split over two chains.
+// block) of activation row b.
 template <int XT, int BATCH, typename XUnit>
 __device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, bool valid, XUnit xunit,
                                           float (&acc)[BATCH]) {
@@ -277,18 +277,18 @@ __device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, bool val
     for (int cc = 0; cc < 4; ++cc) xc[cc] = xunit(b, cc);
     const uint32_t x0[8] = {xc[0].x, xc[0].y, xc[0].z, xc[0].w, xc[1].x, xc[1].y, xc[1].z, xc[1].w};
     const uint32_t x1[8] = {xc[2].x, xc[2].y, xc[2].z, xc[2].w, xc[3].x, xc[3].y, xc[3].z, xc[3].w};
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+    // One fp32 chain per 16-weight half (two chains per half, joined at the end,
+    // measured 1-4 % slower on most decode shapes: two more instructions per block).
+    float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 8; ++t) {
       p0 = A::dot(wl[t], x0[t], p0);
       p1 = A::dot(wh[t], x1[t], p1);
-      p2 = A::dot(wl[t + 4], x0[t + 4], p2);
-      p3 = A::dot(wh[t + 4], x1[t + 4], p3);
     }
     // A masked lane adds nothing: its products may be 0 * inf = NaN, so they are
     // dropped, not scaled by zero.
-    acc[b] = __builtin_fmaf(s0, valid ? p0 + p2 : 0.f, acc[b]);
-    acc[b] = __builtin_fmaf(s1, valid ? p1 + p3 : 0.f, acc[b]);
+    acc[b] = __builtin_fmaf(s0, valid ? p0 : 0.f, acc[b]);
+    acc[b] = __builtin_fmaf(s1, valid ? p1 : 0.f, acc[b]);
   }
 }
 
