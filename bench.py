@@ -12,8 +12,11 @@ Also measured in the same run (reported under "gemm" and "extra"): the prefill G
 (2048 x 17408 x 5120, bf16, TFLOP/s), the up-projection GEMV at batch 2/4/8 (matrix
 cores), the fast-layout down-projection GEMV at batch 1/2/4/8 (bf16), dequantization,
 encoding, and the 64-layer decode sweep (448 GEMVs, 12.3 GB).
-Per-kernel durations come from HIP events recorded around every launch on the stream
-the kernel runs on. The CPU baseline times the fp64 oracle on the host.
+The GEMV extras (batched, down-projection, fused) are timed as HIP graphs of 100
+launches replayed back to back (event time of a replay / 100), so that the GPU never
+waits for the host between these short kernels; the longer kernels (GEMM, dequant,
+encoder) by HIP events around every launch on the stream they run on. The CPU baseline
+times the fp64 oracle on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-sweep]
 """
@@ -72,6 +75,37 @@ def timed_launches(torch, fn, count):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     return [s.elapsed_time(e) for s, e in ev]
+
+
+def graph_us(torch, fn, launches, replays=5):
+    """Mean device time per call of fn(i), i < launches, with the GPU never waiting for
+    the host: the calls are captured in one HIP graph on a stream that one eager call
+    has set up first (per-stream workspaces exist before the capture, so the graph runs
+    the eager plan), then replayed back to back; the mean over replays of
+    (event time of one replay) / launches."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(launches):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / launches)
+    del g
+    return float(np.mean(per))
 
 
 def warm_up(torch, fn, seconds=0.3):
@@ -246,13 +280,12 @@ def main():
     for b in (2, 4, 8):
         xb = xs_host[:b].contiguous().to(dev)
         yb = torch.empty((b, n), dtype=torch.float32, device=dev)
-        for i in range(10):
-            R.rfp4_gemv(copies[i % nc], layout, n, k, xb, yb)
-        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemv(copies[i % nc], layout, n, k, xb, yb), 100))
+        fn = lambda i: R.rfp4_gemv(copies[i % nc], layout, n, k, xb, yb)
+        warm_up(torch, fn, 0.1)
+        us = graph_us(torch, fn, 100)
         bts = w_bytes + b * k * 2 + b * n * 4
-        up_batched[f"b{b}"] = {"GB/s": round(bts / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": bts,
-                               **{kk: round(v, 2) for kk, v in d.items()}}
-        log(f"gemv up b={b}: mean {d['mean_us']:.2f} us -> {up_batched[f'b{b}']['GB/s']:.0f} GB/s")
+        up_batched[f"b{b}"] = {"GB/s": round(bts / (us * 1e-6) / 1e9, 1), "bytes": bts, "mean_us": round(us, 2)}
+        log(f"gemv up b={b}: {us:.2f} us/launch (graph) -> {up_batched[f'b{b}']['GB/s']:.0f} GB/s")
     extra["gemv_up_dual_f16_batched"] = up_batched
     del copies
     torch.cuda.empty_cache()
@@ -266,12 +299,12 @@ def main():
     for b in (1, 2, 4, 8):
         xb = xd_host[:b].contiguous().to(dev)
         yb = torch.empty((b, dn), dtype=torch.float32, device=dev)
-        for i in range(10):
-            R.rfp4_gemv(dcopies[i % len(dcopies)], dl, dn, dk, xb, yb)
-        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemv(dcopies[i % len(dcopies)], dl, dn, dk, xb, yb), 100))
+        fn = lambda i: R.rfp4_gemv(dcopies[i % len(dcopies)], dl, dn, dk, xb, yb)
+        warm_up(torch, fn, 0.1)
+        us = graph_us(torch, fn, 100)
         bts = dw_bytes + b * dk * 2 + b * dn * 4
-        down[f"b{b}"] = {"GB/s": round(bts / (d["mean_us"] * 1e-6) / 1e9, 1), "bytes": bts, **{kk: round(v, 2) for kk, v in d.items()}}
-        log(f"gemv down b={b}: mean {d['mean_us']:.2f} us -> {down[f'b{b}']['GB/s']:.0f} GB/s")
+        down[f"b{b}"] = {"GB/s": round(bts / (us * 1e-6) / 1e9, 1), "bytes": bts, "mean_us": round(us, 2)}
+        log(f"gemv down b={b}: {us:.2f} us/launch (graph) -> {down[f'b{b}']['GB/s']:.0f} GB/s")
     extra["gemv_down_fast_bf16"] = down
     del dcopies
     torch.cuda.empty_cache()
@@ -352,14 +385,15 @@ def main():
         call_f = lambda i: R.rfp4_gemv_multi(sets[i % len(sets)], 0, parts, fk, xf, yfs)
         call_s = lambda i: [R.rfp4_gemv(w, 0, n, fk, xf, y) for w, n, y in zip(sets[i % len(sets)], parts, yfs)]
         warm_up(torch, call_f, 0.1)
-        df = stats_us(timed_launches(torch, call_f, 100))
-        ds = stats_us(timed_launches(torch, call_s, 100))
+        warm_up(torch, call_s, 0.1)
+        uf = graph_us(torch, call_f, 100)
+        us_ = graph_us(torch, call_s, 100)
         bts = total_w + fk * 2 + sum(parts) * 4
         fused[fname] = {"parts": parts, "bytes": bts,
-                        "fused_GB/s": round(bts / (df["mean_us"] * 1e-6) / 1e9, 1), "fused_mean_us": round(df["mean_us"], 2),
-                        "separate_GB/s": round(bts / (ds["mean_us"] * 1e-6) / 1e9, 1), "separate_mean_us": round(ds["mean_us"], 2)}
-        log(f"gemv {fname}: fused {df['mean_us']:.2f} us -> {fused[fname]['fused_GB/s']:.0f} GB/s; "
-            f"separate {ds['mean_us']:.2f} us -> {fused[fname]['separate_GB/s']:.0f} GB/s")
+                        "fused_GB/s": round(bts / (uf * 1e-6) / 1e9, 1), "fused_mean_us": round(uf, 2),
+                        "separate_GB/s": round(bts / (us_ * 1e-6) / 1e9, 1), "separate_mean_us": round(us_, 2)}
+        log(f"gemv {fname}: fused {uf:.2f} us (graph) -> {fused[fname]['fused_GB/s']:.0f} GB/s; "
+            f"separate {us_:.2f} us -> {fused[fname]['separate_GB/s']:.0f} GB/s")
         del sets
         torch.cuda.empty_cache()
     extra["gemv_multi"] = fused
