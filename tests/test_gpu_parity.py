@@ -934,7 +934,8 @@ def test_gemv_mfma_zero_scales_give_zero(monkeypatch):
 
 def test_graph_replay_matches_eager(monkeypatch):
     """Every entry point captured into one HIP graph (batch-1 and batch-4 GEMV, a
-    batch-4 GEMV on long rows whose tiles split, a GEMM with split k, dequant, encoder)
+    batch-4 GEMV on long rows whose tiles split, fused two-matrix GEMVs at batch 1 and
+    4, a GEMM with split k, dequant, encoder)
     and replayed three times, with eager work between the replays, gives exactly the
     eager results. Everything runs on the capture stream first so that the workspaces
     exist before the capture, as the header asks."""
@@ -950,7 +951,13 @@ def test_graph_replay_matches_eager(monkeypatch):
     ws_layout, ws_n, ws_k = 1, 520, 12288  # long rows: the batch-4 GEMV splits its tiles
     wsd = dev(synth.weights(rng, ws_layout, ws_n, ws_k))
     xs4 = synth.activations(rng, 4, ws_k, "bf16").to(DEV).contiguous()
+    mn = [300, 170]  # fused parts sharing the activations
+    wms = [dev(synth.weights(rng, layout, m, k)) for m in mn]
     outs = {"ys": torch.empty((4, ws_n), dtype=torch.float32, device=DEV),
+            "m1a": torch.empty((1, mn[0]), dtype=torch.float32, device=DEV),
+            "m1b": torch.empty((1, mn[1]), dtype=torch.float32, device=DEV),
+            "m4a": torch.empty((4, mn[0]), dtype=torch.float32, device=DEV),
+            "m4b": torch.empty((4, mn[1]), dtype=torch.float32, device=DEV),
             "y1": torch.empty((1, n), dtype=torch.float32, device=DEV),
             "y4": torch.empty((4, n), dtype=torch.float32, device=DEV),
             "c": torch.empty((200, n), dtype=torch.bfloat16, device=DEV),
@@ -961,6 +968,8 @@ def test_graph_replay_matches_eager(monkeypatch):
         R.rfp4_gemv(wsd, ws_layout, ws_n, ws_k, xs4, y=outs["ys"])
         R.rfp4_gemv(wd, layout, n, k, x1, y=outs["y1"])
         R.rfp4_gemv(wd, layout, n, k, x4, y=outs["y4"])
+        R.rfp4_gemv_multi(wms, layout, mn, k, x1, [outs["m1a"], outs["m1b"]])
+        R.rfp4_gemv_multi(wms, layout, mn, k, x4, [outs["m4a"], outs["m4b"]])
         R.rfp4_gemm(wd, layout, n, k, a, c=outs["c"])
         R.rfp4_dequant(wd, layout, n, k, out=outs["d"])
         R.rfp4_quantize(src, layout, out=outs["q"])
