@@ -42,7 +42,7 @@ ROTATE_MIN_BYTES = 600 * 2**20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_up.json")
 GEMV_SOURCES = ["gemm_rfp4_block_amd/csrc/gemv_impl.h", "gemm_rfp4_block_amd/csrc/gemv_mfma.h",
                 "gemm_rfp4_block_amd/csrc/gemv_f16.hip", "gemm_rfp4_block_amd/csrc/gemv.hip",
-                "gemm_rfp4_block_amd/csrc/rfp4_decode.h"]
+                "gemm_rfp4_block_amd/csrc/rfp4_decode.h", "gemm_rfp4_block_amd/csrc/gemv_tall.h"]
 
 
 def log(*a):

@@ -309,6 +309,77 @@ def test_gemv_nonfinite_activations(case, monkeypatch):
         assert O.normalized_error(y[rows], y_ref[rows], den[rows]) <= TOL
 
 
+TALL_CASES = [  # row counts of the matrices (one launch), k, activation dtype, layout
+    ([48], 5120, "f16", 0),             # three tiles
+    ([16], 6144, "f16", 0),             # one tile, six units per lane
+    ([160], 5120, "f16", 0),
+    ([32, 48, 16], 5120, "f16", 0),     # fused parts (tiles map to matrices)
+    ([64, 16], 6144, "f16", 0),
+    ([40], 5120, "f16", 0),             # rows not a multiple of 16: dot-product kernel
+    ([48], 4096, "f16", 0),             # k outside {5120, 6144}: dot-product kernel
+    ([48], 5120, "f16", 1),             # fast layout: dot-product kernel
+    ([48], 5120, "bf16", 0),            # bf16 activations: dot-product kernel
+]
+
+
+@pytest.mark.parametrize("case", TALL_CASES, ids=lambda c: "n{}k{}{}L{}".format("-".join(map(str, c[0])), *c[1:]))
+def test_gemv_tall_forced(case, monkeypatch):
+    """The batch-1 matrix-core kernel for tall launches, forced on wherever the shape
+    allows (RFP4_GEMV_TALL=1), against the oracle; shapes it does not take fall back to
+    the dot-product kernel and must stay correct. Weights include 2 % stress blocks
+    (extreme codes and scales)."""
+    monkeypatch.setenv("RFP4_GEMV_TALL", "1")
+    ns, k, dt, layout = case
+    rng = np.random.default_rng(9900 + sum(ns) + k + layout)
+    ws = [synth.weights(rng, layout, n, k, stress_frac=0.02) for n in ns]
+    x = synth.activations(rng, 1, k, dt)
+    xd = x.to(DEV).contiguous()
+    if len(ns) == 1:
+        ys = [R.rfp4_gemv(dev(ws[0]), layout, ns[0], k, xd)]
+    else:
+        ys = R.rfp4_gemv_multi([dev(w) for w in ws], layout, ns, k, xd)
+    for w, n, y in zip(ws, ns, ys):
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
+
+
+def test_gemv_tall_nonfinite_activations(monkeypatch):
+    """Tall kernel: an infinite activation in the last unit of the rows gives exactly the
+    oracle's +-inf or NaN (a zero weight or a zero scale meeting it); the zero-padded A
+    rows add nothing."""
+    monkeypatch.setenv("RFP4_GEMV_TALL", "1")
+    layout, n, k = 0, 64, 5120
+    rng = np.random.default_rng(9950)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.05)
+    x = synth.activations(rng, 1, k, "f16")
+    x[0, k - 1] = float("inf")
+    x[0, k - 40] = float("-inf")
+    y = R.rfp4_gemv(dev(w), layout, n, k, x.to(DEV).contiguous()).cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
+    assert np.array_equal(np.isnan(y), np.isnan(y_ref))
+    inf = np.isinf(y_ref)
+    assert np.array_equal(y[inf], y_ref[inf])
+    fin = np.isfinite(y_ref)
+    if fin.any():
+        assert np.max(np.abs(y[fin] - y_ref[fin]) / den[fin]) <= TOL
+
+
+def test_gemv_tall_default_fused_gate_up_sampled():
+    """By default a fused gate + up launch (2 x 17408 x 5120, dual, f16, batch 1: >= 8
+    tiles per CU) takes the tall kernel; checked on seeded sampled rows of both matrices
+    (first and last rows included)."""
+    layout, n, k = 0, 17408, 5120
+    rng = np.random.default_rng(9960)
+    ws = [synth.weights(rng, layout, n, k) for _ in range(2)]
+    x = synth.activations(rng, 1, k, "f16")
+    ys = R.rfp4_gemv_multi([dev(w) for w in ws], layout, [n, n], k, x.to(DEV).contiguous())
+    for w, y in zip(ws, ys):
+        rows = np.unique(np.concatenate([[0, 1, 15, 16, n - 17, n - 16, n - 1], rng.choice(n, 64, replace=False)]))
+        y_ref, den = O.gemv_rows(w, layout, n, k, x64(x), rows)
+        assert O.normalized_error(y.cpu().numpy()[:, rows], y_ref, den) <= TOL
+
+
 def test_gemv_zero_scales_give_zero():
     rng = np.random.default_rng(31)
     n, k = 64, 1024
@@ -1022,12 +1093,14 @@ def test_gemv_split_two_streams(monkeypatch):
             assert torch.equal(ys[s][rep], ys[s][0])
 
 
-@pytest.mark.parametrize("mode,batch", [("0", 1), ("1", 4), ("1", 8)])
+@pytest.mark.parametrize("mode,batch", [("0", 1), ("", 1), ("1", 4), ("1", 8)])
 def test_gemv_vocab_rows_sampled(mode, batch, monkeypatch):
     """A vocabulary-sized matrix (152064 x 5120 dual, 438 MB packed: the decode LM head)
-    on either kernel, checked on a seeded sample of rows that includes the first and the
-    last."""
-    monkeypatch.setenv("RFP4_GEMV_MFMA", mode)
+    on each kernel (batch 1: the dot-product kernel forced, and the default, the tall
+    matrix-core kernel), checked on a seeded sample of rows that includes the first and
+    the last."""
+    if mode:
+        monkeypatch.setenv("RFP4_GEMV_MFMA", mode)
     layout, n, k = 0, 152064, 5120
     rng = np.random.default_rng(9700 + batch)
     w = synth.weights(rng, layout, n, k)
