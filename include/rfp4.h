@@ -118,7 +118,11 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n. Batch 1 runs a
  * dot-product kernel, batches from 2 on a matrix-core kernel (the summation order,
  * hence the last bits, differ between the two); the environment variable
- * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. On long rows
+ * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. Batch-1 launches
+ * of at least 8 tiles of 16 rows per CU with the dual layout, f16 activations, k = 5120
+ * or 6144 and every matrix's rows a multiple of 16 run a third, matrix-core kernel for
+ * tall launches (again other last bits); RFP4_GEMV_TALL = "0" or "1" turns it off or
+ * on wherever the shape allows, and RFP4_GEMV_MFMA = "0" turns it off. On long rows
  * (at least 12 chunks of 16 units, a unit being two blocks when k / 32 is even and one
  * otherwise: k >= 11328 or k >= 5664) with fewer than four 16-row tiles per CU the
  * matrix-core kernel gives
