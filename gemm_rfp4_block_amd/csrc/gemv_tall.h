@@ -24,7 +24,7 @@
 // the four activations that meet that word's codes of half h in the slots where B has
 // them, zeros in the other four slots; lanes whose A row is not the current (group,
 // block) read a zero piece. Per 64 weights this takes ~120 VALU instructions against
-// ~146 for the dot-product form; measured faster on launches of >= 8 tiles per CU.
+// ~146 for the dot-product form (which launches it takes: gemv_tall_fits).
 //
 // Requirements (checked by gemv_tall_fits): dual layout, f16 activations, batch 1,
 // k = 1024 * NUL with NUL in {5, 6} (the activations of a 16-lane-group split take
@@ -167,7 +167,11 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
 
 // Whether a batch-1 launch takes the tall kernel. RFP4_GEMV_TALL = 0 / 1 turns it off /
 // on wherever the shape allows (tests); RFP4_GEMV_MFMA = 0 (the dot-product kernel
-// forced) turns it off. By default: launches of at least 8 tiles per CU.
+// forced) turns it off. By default, from timings against the dot-product kernel on one
+// machine: k = 5120 only (at k = 6144 it was 7-10 % slower from 12288 rows), at least
+// two tiles per CU, and the busiest CU at most 7 % above the average tile count (at
+// 17408 rows, 4.25 tiles per CU, it was 2-5 % slower; with even tile counts from 2 to
+// 8.5 per CU it tied or won by up to 9 %).
 inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb, int batch) {
   if (layout != kDual || batch != 1 || (nb != 160 && nb != 192)) return false;
   int64_t tiles = 0;
@@ -181,7 +185,10 @@ inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb,
   const char* mf = getenv("RFP4_GEMV_MFMA");
   if (mf != nullptr && mf[0] == '0') return false;
   if (env != nullptr && env[0] == '1') return true;
-  return tiles >= 8 * static_cast<int64_t>(device_cu_count());
+  if (nb != 160) return false;
+  const int64_t cus = device_cu_count();
+  const int64_t busiest = (tiles + cus - 1) / cus;
+  return tiles >= 2 * cus && busiest * cus * 100 <= tiles * 107;
 }
 
 inline hipError_t launch_gemv_tall(const GemvPart* parts, int count, int nb, const uint16_t* x,

@@ -119,10 +119,11 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * dot-product kernel, batches from 2 on a matrix-core kernel (the summation order,
  * hence the last bits, differ between the two); the environment variable
  * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. Batch-1 launches
- * of at least 8 tiles of 16 rows per CU with the dual layout, f16 activations, k = 5120
- * or 6144 and every matrix's rows a multiple of 16 run a third, matrix-core kernel for
- * tall launches (again other last bits); RFP4_GEMV_TALL = "0" or "1" turns it off or
- * on wherever the shape allows, and RFP4_GEMV_MFMA = "0" turns it off. On long rows
+ * with the dual layout, f16 activations, k = 5120 and every matrix's rows a multiple of
+ * 16, of at least two 16-row tiles per CU spread evenly over the CUs (the busiest at
+ * most 7 % above the average), run a third, matrix-core kernel (again other last
+ * bits); RFP4_GEMV_TALL = "0" or "1" turns it off, or on wherever the shape allows
+ * (k = 5120 or 6144), and RFP4_GEMV_MFMA = "0" turns it off. On long rows
  * (at least 12 chunks of 16 units, a unit being two blocks when k / 32 is even and one
  * otherwise: k >= 11328 or k >= 5664) with fewer than four 16-row tiles per CU the
  * matrix-core kernel gives

@@ -365,6 +365,20 @@ def test_gemv_tall_nonfinite_activations(monkeypatch):
         assert np.max(np.abs(y[fin] - y_ref[fin]) / den[fin]) <= TOL
 
 
+def test_gemv_tall_default_fused_qkv():
+    """By default a fused q + k + v launch (6144 + 1024 + 1024 rows x 5120, dual, f16,
+    batch 1: two 16-row tiles per CU) takes the tall kernel; every row of every part
+    against the oracle."""
+    layout, k, ns = 0, 5120, [6144, 1024, 1024]
+    rng = np.random.default_rng(9970)
+    ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
+    x = synth.activations(rng, 1, k, "f16")
+    ys = R.rfp4_gemv_multi([dev(w) for w in ws], layout, ns, k, x.to(DEV).contiguous())
+    for w, n, y in zip(ws, ns, ys):
+        y_ref, den = O.gemv(w, layout, n, k, x64(x))
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
+
+
 def test_gemv_tall_default_fused_gate_up_sampled():
     """By default a fused gate + up launch (2 x 17408 x 5120, dual, f16, batch 1: >= 8
     tiles per CU) takes the tall kernel; checked on seeded sampled rows of both matrices
