@@ -148,7 +148,7 @@ def bench_gemv_graph(torch, R, copies, layout, n, k, x, y, steps, warmup):
         R.rfp4_gemv(copies[0], layout, n, k, x, y)  # warm the capture stream
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):
         for i in range(steps):
             R.rfp4_gemv(copies[i % nc], layout, n, k, x, y)
     g.replay()  # untimed replay, checked below against the eager result
@@ -423,7 +423,7 @@ def main():
             sweep()
         torch.cuda.current_stream().wait_stream(s2)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=s2):
             sweep()
         g.replay()
         torch.cuda.synchronize()
@@ -464,7 +464,7 @@ def main():
             fsweep()
         torch.cuda.current_stream().wait_stream(s3)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g2):
+        with torch.cuda.graph(g2, stream=s3):
             fsweep()
         g2.replay()
         torch.cuda.synchronize()
