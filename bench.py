@@ -43,6 +43,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_up.json")
 GEMV_SOURCES = ["gemm_rfp4_block_amd/csrc/gemv_impl.h", "gemm_rfp4_block_amd/csrc/gemv_mfma.h",
                 "gemm_rfp4_block_amd/csrc/gemv_f16.hip", "gemm_rfp4_block_amd/csrc/gemv.hip",
                 "gemm_rfp4_block_amd/csrc/rfp4_decode.h", "gemm_rfp4_block_amd/csrc/gemv_tall.h"]
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_prefill.json")
+GEMM_SOURCES = ["gemm_rfp4_block_amd/csrc/gemm.hip", "gemm_rfp4_block_amd/csrc/rfp4_decode.h",
+                "gemm_rfp4_block_amd/csrc/rfp4_internal.h"]
 
 
 def log(*a):
@@ -206,8 +209,13 @@ def main():
         c = torch.empty((gcfg["m"], gcfg["n"]), dtype=torch.bfloat16, device=dev)
         for _ in range(8):
             R.rfp4_gemm(wg, gcfg["layout"], gcfg["n"], gcfg["k"], a, c)
+        # a plain device copy of known size calibrates the HBM byte counters
+        src = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        log("pmc gemm mode done: 8 prefill GEMM launches")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"pmc gemm mode done: 8 prefill GEMM launches, one copy of {src.numel()} bytes")
         return
 
     # ---------------- headline: up-projection GEMV, dual, fp16, batch 1
@@ -354,9 +362,18 @@ def main():
         d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c), 50))
         flops = 2.0 * gm * gn * gk
         tf = flops / (d["mean_us"] * 1e-6) / 1e12
+        # L2 <-> fabric bytes of one call (its three launches), from the FETCH_SIZE and
+        # WRITE_SIZE counters scaled by a plain copy's readings; only while the GEMM
+        # sources are the ones the counters were taken on
+        gtraffic = None
+        if os.path.exists(GEMM_TRAFFIC_FILE):
+            with open(GEMM_TRAFFIC_FILE) as f:
+                tr = json.load(f)
+            if tr.get("source_hash") == source_hash(GEMM_SOURCES):
+                gtraffic = tr.get("bytes_per_call")
         gemm = {"TFLOP/s": round(tf, 1), "flop": flops, "m": gm, "n": gn, "k": gk,
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": gtraffic},
                 **{kk: round(v, 2) for kk, v in d.items()}}
         log(f"gemm: mean {d['mean_us']:.1f} us -> {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
         # the dequantize-then-multiply baseline (bf16 expansion + rocBLAS dense GEMM)
