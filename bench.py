@@ -98,6 +98,7 @@ def graph_us(torch, fn, launches, replays=5):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
+    settle_graph(torch, g, 0.2)
     stream = torch.cuda.current_stream()
     per = []
     for _ in range(replays):
@@ -109,6 +110,15 @@ def graph_us(torch, fn, launches, replays=5):
         per.append(e0.elapsed_time(e1) * 1e3 / launches)
     del g
     return float(np.mean(per))
+
+
+def settle_graph(torch, g, seconds):
+    """Replay g untimed until `seconds` of wall time have passed: capturing a graph leaves
+    the GPU idle long enough for its clocks to drop below their loaded level."""
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
 
 
 def warm_up(torch, fn, seconds=0.3):
@@ -157,6 +167,7 @@ def bench_gemv_graph(torch, R, copies, layout, n, k, x, y, steps, warmup):
     g.replay()  # untimed replay, checked below against the eager result
     torch.cuda.synchronize()
     replay_ok = bool(torch.equal(y, eager_ref))
+    settle_graph(torch, g, 0.3)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -444,6 +455,7 @@ def main():
             sweep()
         g.replay()
         torch.cuda.synchronize()
+        settle_graph(torch, g, 0.3)
         reps = 5
         t0 = time.perf_counter()
         for _ in range(reps):
@@ -485,6 +497,7 @@ def main():
             fsweep()
         g2.replay()
         torch.cuda.synchronize()
+        settle_graph(torch, g2, 0.3)
         t0 = time.perf_counter()
         for _ in range(reps):
             g2.replay()
