@@ -7,9 +7,11 @@ Host-side row validation is compared with the oracle's.
 """
 
 import ctypes
+import json
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -236,3 +238,13 @@ def test_validate_matches_oracle(L, layout):
         st, bad = R.rfp4_validate(flat, layout, n, k)
         assert not ok
         assert st == R.RFP4_ERR_NONFINITE_SCALE and bad == first
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for several, it prints one JSON line naming the
+    reason and exits with status 2 before touching a device."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in line["error"]
