@@ -1,6 +1,6 @@
 // Fused dequant + GEMV for decode: y[b][r] = sum_c W[r][c] * x[b][c], batch 1..8 (the
-// dot-product kernel; batches from 2 on default to the matrix-core kernel of
-// gemv_mfma.h).
+// dot-product kernel; larger batches default to the matrix-core kernel of gemv_mfma.h
+// as use_mfma there decides).
 //
 // The page names gemv as the decode hot path ("Feasibility Report: Porting ROCmFP4
 // to Atlas", "Kernel System" and "Integration Options", Option 2) and says that on

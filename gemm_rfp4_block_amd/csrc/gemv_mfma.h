@@ -449,21 +449,29 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
                 : launch_mfma_p<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream);
 }
 
-// Matrix-core path for the batches where it is faster: measured on the decode shapes,
-// the dot-product kernel wins at batch 1 (12.5 against 14.7 us at 17408 x 5120: its
-// decode needs no table, no staging and no cross-wave reduction) and the matrix cores
-// from batch 2 on (15.7 against 16.6 us there; the dot-product work grows with the
-// batch, the decode here does not). The environment variable RFP4_GEMV_MFMA = "0"
-// selects the dot-product kernel and "1" the matrix cores for every batch; otherwise
-// batches >= RFP4_GEMV_MFMA_MIN_BATCH take the matrix cores.
+// Matrix-core path for the launches where it is faster. Measured on the decode shapes
+// (graph-replayed launches over rotating weight copies, one machine): the dot-product
+// kernel wins at batch 1 (12.5 against 14.7 us at 17408 x 5120: its decode needs no
+// table, no staging and no cross-wave reduction) and still at batch 2 on long rows or
+// many rows (17408 x 5120 16.15 / 16.84 us, 5120 x 17408 19.59 / 20.05, 5120 x 6144
+// 9.63 / 10.12, dot-product / matrix cores) but not on 6144 x 5120 (9.24 / 9.02); from
+// batch 3 the matrix cores win on all four (their decode does not grow with the batch).
+// The environment variable RFP4_GEMV_MFMA = "0" selects the dot-product kernel and "1"
+// the matrix cores for every launch.
 #ifndef RFP4_GEMV_MFMA_MIN_BATCH
 #define RFP4_GEMV_MFMA_MIN_BATCH 2
 #endif
-inline bool use_mfma(int batch) {
+inline bool use_mfma(const GemvPart* parts, int count, int nb, int batch) {
   const char* env = getenv("RFP4_GEMV_MFMA");
   if (env != nullptr && env[0] == '0') return false;
   if (env != nullptr && env[0] == '1') return true;
-  return batch >= RFP4_GEMV_MFMA_MIN_BATCH;
+  if (batch < RFP4_GEMV_MFMA_MIN_BATCH) return false;
+  if (batch == 2) {
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) rows += parts[i].n;
+    if (nb >= 192 || rows >= 16384) return false;
+  }
+  return true;
 }
 
 template <int XT>
