@@ -454,8 +454,10 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
 // kernel wins at batch 1 (12.5 against 14.7 us at 17408 x 5120: its decode needs no
 // table, no staging and no cross-wave reduction) and still at batch 2 on long rows or
 // many rows (17408 x 5120 16.15 / 16.84 us, 5120 x 17408 19.59 / 20.05, 5120 x 6144
-// 9.63 / 10.12, dot-product / matrix cores) but not on 6144 x 5120 (9.24 / 9.02); from
-// batch 3 the matrix cores win on all four (their decode does not grow with the batch).
+// 9.63 / 10.12, dot-product / matrix cores) but not on 6144 x 5120 (9.24 / 9.02), fused
+// q + k + v (9.75 / 10.15 with the dot-product kernel) or fused gate + up, 34816 rows
+// (28.0 / 29.9), where the matrix-core tiles fill the CUs evenly; from batch 3 the
+// matrix cores win on all of these (their decode does not grow with the batch).
 // The environment variable RFP4_GEMV_MFMA = "0" selects the dot-product kernel and "1"
 // the matrix cores for every launch.
 #ifndef RFP4_GEMV_MFMA_MIN_BATCH
@@ -469,7 +471,7 @@ inline bool use_mfma(const GemvPart* parts, int count, int nb, int batch) {
   if (batch == 2) {
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += parts[i].n;
-    if (nb >= 192 || rows >= 16384) return false;
+    if ((nb >= 192 || rows >= 16384) && rows < 32768) return false;
   }
   return true;
 }

@@ -117,8 +117,8 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * with x of dtype xdtype (RFP4_F16 or RFP4_BF16), products formed exactly and summed
  * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n. Batch 1 runs a
  * dot-product kernel, batches from 3 on a matrix-core kernel, batch 2 the dot-product
- * kernel when k >= 6144 or the launch has >= 16384 rows in all and the matrix-core
- * kernel otherwise (the summation order, hence the last bits, differ between the
+ * kernel when k >= 6144 or the launch has >= 16384 rows in all, and fewer than 32768
+ * rows, the matrix-core kernel otherwise (the summation order, hence the last bits, differ between the
  * two); the environment variable
  * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. Batch-1 launches
  * with the dual layout, f16 activations, k = 5120 and every matrix's rows a multiple of
