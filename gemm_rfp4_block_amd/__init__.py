@@ -28,8 +28,31 @@ RFP4_ERR_HIP = 5
 
 EXPORTED = ("rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
             "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
-            "rfp4_gemm_dequant", "rfp4_quantize")
+            "rfp4_gemm_dequant", "rfp4_quantize", "rfp4_gemv_multi_ex", "rfp4_gemm_ex")
 MAX_GEMV_PARTS = 8
+
+# rfp4_gemv_kernel and rfp4_gemm_plan (include/rfp4.h)
+GEMV_KERNEL = {"auto": 0, "dot": 1, "tiles": 2, "tall": 3, "no_tall": 4}
+GEMM_PLAN = {"auto": 0, "main": 1, "msplit2": 2, "msplit3": 3, "msplit4": 4, "tail": 5, "tail2": 6,
+             "tail4": 7, "nosplit": 8}
+
+
+class Force(ctypes.Structure):
+    """struct rfp4_force: kernel and plan overrides of the _ex entry points (all zero =
+    the library's own choices)."""
+
+    _fields_ = [("gemv_kernel", ctypes.c_int32), ("gemv_unit_blocks", ctypes.c_int32),
+                ("gemv_lanes_per_row", ctypes.c_int32), ("gemv_splits", ctypes.c_int32),
+                ("gemm_plan", ctypes.c_int32)]
+
+
+def make_force(gemv_kernel: str = "auto", gemv_plan: tuple | None = None, gemv_splits: int = 0,
+               gemm_plan: str = "auto") -> Force:
+    """An rfp4_force from names: gemv_kernel in GEMV_KERNEL, gemv_plan = (blocks per lane
+    unit, lanes per row) of the dot-product kernel, gemv_splits of the tile kernel,
+    gemm_plan in GEMM_PLAN."""
+    p, cl = gemv_plan if gemv_plan is not None else (0, 0)
+    return Force(GEMV_KERNEL[gemv_kernel], p, cl, gemv_splits, GEMM_PLAN[gemm_plan])
 
 
 class Rfp4Error(RuntimeError):
@@ -73,6 +96,12 @@ def lib() -> ctypes.CDLL:
     L.rfp4_gemv_multi.restype = c_int
     L.rfp4_gemm.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]
     L.rfp4_gemm.restype = c_int
+    fp = ctypes.POINTER(Force)
+    L.rfp4_gemv_multi_ex.argtypes = [c_int, ctypes.POINTER(c_vp), ctypes.POINTER(c_i64), c_int, c_i64, c_vp,
+                                     c_int, c_i64, c_i64, ctypes.POINTER(c_vp), ctypes.POINTER(c_i64), fp, c_vp]
+    L.rfp4_gemv_multi_ex.restype = c_int
+    L.rfp4_gemm_ex.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, fp, c_vp]
+    L.rfp4_gemm_ex.restype = c_int
     L.rfp4_dequant_bf16.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_vp]
     L.rfp4_dequant_bf16.restype = c_int
     L.rfp4_gemm_dequant.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]
@@ -160,8 +189,9 @@ def rfp4_dequant_bf16(w, layout: int, n: int, k: int, out=None, stream=None):
     return out
 
 
-def rfp4_gemv(w, layout: int, n: int, k: int, x, y=None, stream=None):
-    """y[b, r] = sum_c W[r, c] x[b, c]; ``x`` (batch, k) f16/bf16 on the device, y fp32."""
+def rfp4_gemv(w, layout: int, n: int, k: int, x, y=None, stream=None, force: Force | None = None):
+    """y[b, r] = sum_c W[r, c] x[b, c]; ``x`` (batch, >= k) f16/bf16 on the device, y fp32
+    (batch, >= n). With ``force`` the call goes to rfp4_gemv_multi_ex."""
     import torch
 
     if x.dim() == 1:
@@ -171,12 +201,16 @@ def rfp4_gemv(w, layout: int, n: int, k: int, x, y=None, stream=None):
         y = torch.empty((batch, n), dtype=torch.float32, device=x.device)
     ldx = x.stride(0) if batch > 1 else max(k, x.stride(0))
     ldy = y.stride(0) if y.dim() == 2 and batch > 1 else max(n, y.stride(0) if y.dim() == 2 else n)
-    _check(lib().rfp4_gemv(_ptr(w), layout, n, k, _ptr(x), _xdtype(x), batch, ldx, _ptr(y), ldy,
-                           _stream(stream)), "rfp4_gemv")
+    if force is None:
+        _check(lib().rfp4_gemv(_ptr(w), layout, n, k, _ptr(x), _xdtype(x), batch, ldx, _ptr(y), ldy,
+                               _stream(stream)), "rfp4_gemv")
+    else:
+        rfp4_gemv_multi([w], layout, [n], k, x, [y], stream=stream, force=force, _ldy=[ldy])
     return y
 
 
-def rfp4_gemv_multi(ws, layout: int, ns, k: int, x, ys=None, stream=None):
+def rfp4_gemv_multi(ws, layout: int, ns, k: int, x, ys=None, stream=None, force: Force | None = None,
+                    _ldy=None):
     """One launch of len(ws) matvecs sharing x: ys[i][b, r] = sum_c Ws[i][r, c] x[b, c]."""
     import torch
 
@@ -187,25 +221,35 @@ def rfp4_gemv_multi(ws, layout: int, ns, k: int, x, ys=None, stream=None):
     if ys is None:
         ys = [torch.empty((batch, int(n)), dtype=torch.float32, device=x.device) for n in ns]
     ldx = x.stride(0) if batch > 1 else max(k, x.stride(0))
-    ldy = [y.stride(0) if batch > 1 else max(int(n), y.stride(0)) for y, n in zip(ys, ns)]
+    ldy = _ldy if _ldy is not None else [y.stride(0) if batch > 1 else max(int(n), y.stride(0))
+                                         for y, n in zip(ys, ns)]
     wa = (ctypes.c_void_p * count)(*[w.data_ptr() for w in ws])
     na = (ctypes.c_int64 * count)(*[int(n) for n in ns])
     ya = (ctypes.c_void_p * count)(*[y.data_ptr() for y in ys])
     la = (ctypes.c_int64 * count)(*ldy)
-    _check(lib().rfp4_gemv_multi(count, wa, na, layout, k, _ptr(x), _xdtype(x), batch, ldx, ya, la,
-                                 _stream(stream)), "rfp4_gemv_multi")
+    if force is None:
+        _check(lib().rfp4_gemv_multi(count, wa, na, layout, k, _ptr(x), _xdtype(x), batch, ldx, ya, la,
+                                     _stream(stream)), "rfp4_gemv_multi")
+    else:
+        _check(lib().rfp4_gemv_multi_ex(count, wa, na, layout, k, _ptr(x), _xdtype(x), batch, ldx, ya, la,
+                                        ctypes.byref(force), _stream(stream)), "rfp4_gemv_multi_ex")
     return ys
 
 
-def rfp4_gemm(w, layout: int, n: int, k: int, a, c=None, stream=None):
-    """C = A W^T with A (m, k) bf16 and C (m, n) bf16 on the device."""
+def rfp4_gemm(w, layout: int, n: int, k: int, a, c=None, stream=None, force: Force | None = None):
+    """C = A W^T with A (m, k) bf16 and C (m, n) bf16 on the device. With ``force`` the
+    call goes to rfp4_gemm_ex."""
     import torch
 
     m = a.shape[0]
     if c is None:
         c = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
-    _check(lib().rfp4_gemm(_ptr(w), layout, n, k, _ptr(a), m, a.stride(0), _ptr(c), c.stride(0),
-                           _stream(stream)), "rfp4_gemm")
+    if force is None:
+        _check(lib().rfp4_gemm(_ptr(w), layout, n, k, _ptr(a), m, a.stride(0), _ptr(c), c.stride(0),
+                               _stream(stream)), "rfp4_gemm")
+    else:
+        _check(lib().rfp4_gemm_ex(_ptr(w), layout, n, k, _ptr(a), m, a.stride(0), _ptr(c), c.stride(0),
+                                  ctypes.byref(force), _stream(stream)), "rfp4_gemm_ex")
     return c
 
 
@@ -246,5 +290,6 @@ __all__ = [
     "RFP4_DUAL", "RFP4_FAST", "RFP4_F16", "RFP4_BF16", "Rfp4Error", "lib", "library_path",
     "rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
     "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
-    "rfp4_gemm_dequant", "rfp4_quantize", "RFP4_F32", "MAX_GEMV_PARTS",
+    "rfp4_gemm_dequant", "rfp4_quantize", "RFP4_F32", "MAX_GEMV_PARTS", "Force", "make_force",
+    "GEMV_KERNEL", "GEMM_PLAN",
 ]

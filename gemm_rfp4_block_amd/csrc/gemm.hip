@@ -15,9 +15,9 @@
 //
 // Balance. A grid of equal tiles runs in whole rounds over the CUs, so 544 tiles on
 // 256 CUs would take three rounds for 2.125 rounds of work. The launcher therefore
-// splits the last columns of tiles into 128 x 64 pieces (a 256-thread configuration,
-// wavefronts of 64 x 32), run by a second launch, choosing the split with a cost model
-// of whole rounds of each kind.
+// computes the last columns of C as 128 x 128 tiles (a 256-thread configuration of four
+// wavefronts, one per SIMD, each owning 64 x 64), run by a second launch, and may split
+// the k range of either kind of tile; a cost model of the launch picks the plan.
 //
 // Pipeline (LDS double-buffered, one barrier per step). While step s is multiplied out
 // of LDS buffer s % 2:
@@ -39,7 +39,6 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
-#include <string>
 #include <type_traits>
 
 #include "rfp4_decode.h"
@@ -843,11 +842,11 @@ inline double rounds(int64_t workgroups, int cus) {
 }
 
 // Chooses the tail strips and the splits of main and tail tiles with the lowest modelled
-// time. RFP4_GEMM_PLAN = "main", "tail", "tail2", "tail4", "msplit2", "msplit3" or
-// "msplit4" forces all-main tiles, all-tail tiles with that split, or all-main tiles
-// with that split (lets tests cover every path at small sizes); "nosplit" chooses among
-// the plans without a split.
-Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
+// time, among plans whose partial sums fit max_partial_bytes. A forced plan (rfp4_force)
+// selects all-main tiles, all-tail tiles with a given split, or all-main tiles with a
+// given split (so tests cover every path at small sizes), or restricts the choice to
+// plans without a split.
+Plan choose_plan(int64_t m, int64_t n, int nb, int cus, int forced, double max_partial_bytes) {
   const int64_t strips = (n + MainCfg::BN - 1) / MainCfg::BN;
   const int64_t mt = (m + MainCfg::BM - 1) / MainCfg::BM;
   const int64_t slabs = (m + TailCfg::BM - 1) / TailCfg::BM;
@@ -857,26 +856,22 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
   };
   const int max_split = (nb + 3) / 4;  // each split needs at least two 64-column steps
   const double k = 32.0 * nb;
-  const char* env = getenv("RFP4_GEMM_PLAN");
-  const std::string plan = env != nullptr ? env : "";
-  if (plan == "main") return Plan{0, 1, 0, 1, mt * strips};
-  if (plan == "msplit2" || plan == "msplit3" || plan == "msplit4")
-    return Plan{0, 1, 0, std::min(plan[6] - '0', max_split), mt * strips};
-  if (plan == "tail" || plan == "tail2" || plan == "tail4") {
-    int sp = plan == "tail" ? 1 : (plan == "tail2" ? 2 : 4);
+  if (forced == RFP4_GEMM_PLAN_MAIN) return Plan{0, 1, 0, 1, mt * strips};
+  if (forced >= RFP4_GEMM_PLAN_MSPLIT2 && forced <= RFP4_GEMM_PLAN_MSPLIT4)
+    return Plan{0, 1, 0, std::min(forced - RFP4_GEMM_PLAN_MSPLIT2 + 2, max_split), mt * strips};
+  if (forced >= RFP4_GEMM_PLAN_TAIL && forced <= RFP4_GEMM_PLAN_TAIL4) {
+    int sp = forced == RFP4_GEMM_PLAN_TAIL ? 1 : (forced == RFP4_GEMM_PLAN_TAIL2 ? 2 : 4);
     if (sp > max_split) sp = max_split;
     return Plan{strips, sp, tail_tiles(strips)};
   }
-  const bool allow_split = plan != "nosplit";
+  const bool allow_split = forced != RFP4_GEMM_PLAN_NOSPLIT;
   auto reduce_us = [](int64_t tiles, int sp, int tile_elems) {
     return sp > 1 ? (static_cast<double>(tiles) * tile_elems * (4.0 * sp + 2.0)) / kReduceBytesPerUs +
                         kReduceFixedUs
                   : 0.0;
   };
-  // Partial sums of one launch stay within kMaxPartialBytes (the workspace is kept).
-  constexpr double kMaxPartialBytes = 512.0 * 1024 * 1024;
   auto partial_ok = [&](int64_t tiles, int sp, int tile_elems) {
-    return sp == 1 || static_cast<double>(tiles) * sp * tile_elems * 4.0 <= kMaxPartialBytes;
+    return sp == 1 || static_cast<double>(tiles) * sp * tile_elems * 4.0 <= max_partial_bytes;
   };
   Plan best{0, 1, 0, 1, mt * strips};
   double best_cost = 1e300;
@@ -896,6 +891,9 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
         const double ct = tt > 0 ? kTailUsPerK * k / sp * rounds(tt * sp, cus) +
                                        reduce_us(tt, sp, TailCfg::BM * TailCfg::BN)
                                  : 0.0;
+        const double pbytes = (spm > 1 ? static_cast<double>(main_tiles) * spm * MainCfg::BM * MainCfg::BN * 4.0 : 0.0) +
+                              (sp > 1 ? static_cast<double>(tt) * sp * TailCfg::BM * TailCfg::BN * 4.0 : 0.0);
+        if (pbytes > max_partial_bytes) continue;
         if (cm + ct < best_cost - 1e-9) {
           best_cost = cm + ct;
           best = Plan{t, sp, tt, spm, main_tiles};
@@ -908,8 +906,16 @@ Plan choose_plan(int64_t m, int64_t n, int nb, int cus) {
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
-                       int64_t m, int64_t lda, uint16_t* c, int64_t ldc, hipStream_t stream) {
+namespace {
+
+// The GEMM over all rows, in chunks of rows so each grid stays within 2^31 workgroups.
+// `get_ws(bytes, &ptr)` provides the partial-sum buffer of a split plan (false: none,
+// and the chunk then runs its plan unsplit); plans are chosen among those whose
+// partial sums fit max_partial_bytes.
+template <typename GetWs>
+hipError_t run_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
+                    int64_t m, int64_t lda, uint16_t* c, int64_t ldc, int forced,
+                    double max_partial_bytes, GetWs get_ws, hipStream_t stream) {
   // Any k % 32 == 0: the kernel runs two 64-column steps per iteration, and when
   // k % 128 != 0 its k-tail variant zero-fills the last pair past k.
   const int nb = static_cast<int>(k / 32);
@@ -917,11 +923,10 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
   if (e != hipSuccess) return e;
   const int cus = device_cu_count();
   const int64_t strips = (n + MainCfg::BN - 1) / MainCfg::BN;
-  // Launch in chunks of rows so each grid stays within 2^31 workgroups.
   const int64_t max_m = int64_t(1) << 20;
   for (int64_t m_off = 0; m_off < m; m_off += max_m) {
     const int mc = static_cast<int>(m - m_off < max_m ? m - m_off : max_m);
-    Plan plan = choose_plan(mc, n, nb, cus);
+    Plan plan = choose_plan(mc, n, nb, cus, forced, max_partial_bytes);
     float* partial = nullptr;       // tail partial sums
     float* partial_main = nullptr;  // main partial sums (before the tail's)
     const size_t main_bytes = plan.main_splits > 1 ? static_cast<size_t>(plan.main_tiles) * plan.main_splits *
@@ -932,8 +937,7 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
                                               : 0;
     if (main_bytes + tail_bytes > 0) {
       float* ws = nullptr;
-      if (stream_workspace(kWorkspaceGemm, stream, main_bytes + tail_bytes, reinterpret_cast<void**>(&ws)) !=
-          hipSuccess) {
+      if (!get_ws(main_bytes + tail_bytes, &ws)) {
         plan.splits = 1;  // no workspace (graph capture or no memory): run every tile unsplit
         plan.main_splits = 1;
       } else {
@@ -952,6 +956,17 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
+                       int64_t m, int64_t lda, uint16_t* c, int64_t ldc, const Force& force,
+                       hipStream_t stream) {
+  auto get_ws = [&](size_t bytes, float** out) {
+    return stream_workspace(kWorkspaceGemm, stream, bytes, false, reinterpret_cast<void**>(out)) == hipSuccess;
+  };
+  return run_gemm(w, layout, n, k, a, m, lda, c, ldc, force.gemm_plan, 512.0 * 1024 * 1024, get_ws, stream);
 }
 
 }  // namespace rfp4

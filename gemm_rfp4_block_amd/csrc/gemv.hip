@@ -2,16 +2,20 @@
 // compiled once per activation dtype in gemv_f16.hip and gemv_bf16.hip).
 
 #include <mutex>
+#include <vector>
 
 #include "rfp4_internal.h"
 
 namespace rfp4 {
 
 // Device workspaces, one per (kind, device, stream): calls ordered on a stream reuse
-// theirs and calls on different streams never share one. A workspace grows on demand
-// (after the stream's earlier work has finished), starts zero-filled and is kept until
-// the process ends. Nothing is allocated while the stream is being captured.
-hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void** out) {
+// theirs and calls on different streams never share one. Nothing here frees memory or
+// synchronizes: a launch that needs more than its stream's workspace holds gets a new
+// buffer (at least twice as large), and the outgrown one stays allocated, unused, until
+// the process ends, because kernels still in flight or graphs captured earlier may
+// write to it. Growth by doubling bounds what is kept to the size of the live buffer.
+// Nothing is allocated while the stream is being captured.
+hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, bool zero, void** out) {
   struct Entry {
     int kind;
     int dev;
@@ -20,44 +24,46 @@ hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void** o
     size_t bytes;
   };
   static std::mutex mu;
-  static Entry entries[256];
-  static int count = 0;
+  static std::vector<Entry> entries;  // live workspaces
+  static std::vector<void*> retired;  // outgrown workspaces, never freed
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
   Entry* en = nullptr;
-  for (int i = 0; i < count; ++i)
-    if (entries[i].kind == kind && entries[i].dev == dev && entries[i].stream == stream) en = &entries[i];
-  if (en == nullptr) {
-    if (count == 256) return hipErrorOutOfMemory;
-    en = &entries[count++];
-    *en = Entry{kind, dev, stream, nullptr, 0};
+  for (Entry& x : entries)
+    if (x.kind == kind && x.dev == dev && x.stream == stream) en = &x;
+  if (en != nullptr && en->bytes >= bytes) {
+    *out = en->ptr;
+    return hipSuccess;
   }
-  if (en->bytes < bytes) {
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cap);
-    if (e != hipSuccess) return e;
-    if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
-    if (en->ptr != nullptr) {
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return e;
-      e = hipFree(en->ptr);
-      en->ptr = nullptr;
-      en->bytes = 0;
-      if (e != hipSuccess) return e;
-    }
-    e = hipMalloc(&en->ptr, bytes);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return e;
+  if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+  size_t want = bytes;
+  if (en != nullptr && want < 2 * en->bytes) want = 2 * en->bytes;
+  void* p = nullptr;
+  e = hipMalloc(&p, want);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // the failed allocation's error is reported here, not later
+    return e;
+  }
+  if (zero) {
+    e = hipMemsetAsync(p, 0, want, stream);
     if (e != hipSuccess) {
-      (void)hipGetLastError();  // the failed allocation's error is reported here, not later
-      en->ptr = nullptr;
+      retired.push_back(p);
       return e;
     }
-    e = hipMemsetAsync(en->ptr, 0, bytes, stream);
-    if (e != hipSuccess) return e;
-    en->bytes = bytes;
   }
-  *out = en->ptr;
+  if (en == nullptr) {
+    entries.push_back(Entry{kind, dev, stream, p, want});
+  } else {
+    retired.push_back(en->ptr);
+    en->ptr = p;
+    en->bytes = want;
+  }
+  *out = p;
   return hipSuccess;
 }
 
@@ -79,11 +85,11 @@ int device_cu_count() {
 }
 
 hipError_t launch_gemv(const GemvPart* parts, int count, int layout, int64_t k, const void* x,
-                       int xdtype, int batch, int64_t ldx, hipStream_t stream) {
+                       int xdtype, int batch, int64_t ldx, const Force& force, hipStream_t stream) {
   const int nb = static_cast<int>(k / 32);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  return xdtype == kF16 ? launch_gemv_f16(parts, count, layout, nb, xp, batch, ldx, stream)
-                        : launch_gemv_bf16(parts, count, layout, nb, xp, batch, ldx, stream);
+  return xdtype == kF16 ? launch_gemv_f16(parts, count, layout, nb, xp, batch, ldx, force, stream)
+                        : launch_gemv_bf16(parts, count, layout, nb, xp, batch, ldx, force, stream);
 }
 
 }  // namespace rfp4

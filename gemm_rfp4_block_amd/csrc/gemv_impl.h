@@ -37,9 +37,6 @@
 
 #pragma once
 
-#include <stdio.h>
-#include <stdlib.h>
-
 #include "rfp4_decode.h"
 #include "rfp4_internal.h"
 
@@ -575,19 +572,15 @@ inline Plan make_plan(int p, int log2cl, const GemvPart* parts, int count, int n
 // pairs of blocks per unit (fewer load instructions) and the fewest lanes per row that
 // still give >= 8 busy wavefronts per CU (CL = gcd(64, units per row) or more, with
 // the remainder masked); with activations read from global memory (long rows), single
-// blocks and 64 lanes per row. RFP4_GEMV_PLAN = "P:CL" (P in {1, 2}, CL a power of two
-// up to 64) forces a mapping.
+// blocks and 64 lanes per row. A forced mapping (rfp4_force: P blocks per unit, CL
+// lanes per row) replaces the choice; a pair mapping on an odd block count is ignored.
 inline Plan choose_plan(const GemvPart* parts, int count, int nb, int waves_per_cu, bool xlds,
-                        int threads) {
-  const char* env = getenv("RFP4_GEMV_PLAN");
-  if (env != nullptr) {
-    int fp = 0, fcl = 0;
-    if (sscanf(env, "%d:%d", &fp, &fcl) == 2 && (fp == 1 || (fp == 2 && nb % 2 == 0)) && fcl >= 1 &&
-        fcl <= 64 && (fcl & (fcl - 1)) == 0) {
-      int l = 0;
-      while ((1 << l) < fcl) ++l;
-      return make_plan(fp, l, parts, count, nb, waves_per_cu, threads);
-    }
+                        int threads, const Force& force) {
+  const int fp = force.gemv_unit_blocks, fcl = force.gemv_lanes_per_row;
+  if (fp != 0 && (fp == 1 || nb % 2 == 0)) {
+    int l = 0;
+    while ((1 << l) < fcl) ++l;
+    return make_plan(fp, l, parts, count, nb, waves_per_cu, threads);
   }
   const int p = (xlds && nb % 2 == 0) ? 2 : 1;
   if (!xlds) return make_plan(1, 6, parts, count, nb, waves_per_cu, threads);
@@ -628,7 +621,7 @@ hipError_t raise_lds_limit(int p) {
 
 template <int LAYOUT, int XT, int BATCH, int NP>
 hipError_t launch3(const GemvPart* parts, int count, int nb, const uint16_t* x, int64_t ldx,
-                   hipStream_t stream) {
+                   const Force& force, hipStream_t stream) {
   // Activation bytes in LDS (largest unit size: 4P+1 units of 16 bytes per P blocks).
   // Long rows are staged in the layout of the units the plan uses: pairs of blocks (9
   // chunks per 2 blocks) when the block count is even, else single blocks (5 per block).
@@ -647,7 +640,7 @@ hipError_t launch3(const GemvPart* parts, int count, int nb, const uint16_t* x, 
     const int wg_fit = static_cast<int>((160 * 1024) / xbytes_fit);
     if (wg_fit * (threads / 64) < waves_per_cu) waves_per_cu = wg_fit * (threads / 64);
   }
-  Plan pl = choose_plan(parts, count, nb, waves_per_cu, xlds, threads);
+  Plan pl = choose_plan(parts, count, nb, waves_per_cu, xlds, threads, force);
   // A forced single-block mapping whose staging layout would not fit takes pairs.
   if (large_x && pl.p == 1 && xbytes1 > static_cast<size_t>(kXLdsBudgetLarge))
     pl = make_plan(2, pl.log2cl, parts, count, nb, waves_per_cu, threads);
@@ -700,28 +693,28 @@ hipError_t launch3(const GemvPart* parts, int count, int nb, const uint16_t* x, 
 
 template <int LAYOUT, int XT, int NP>
 hipError_t launch2(const GemvPart* parts, int count, int nb, const uint16_t* x, int batch,
-                   int64_t ldx, hipStream_t s) {
+                   int64_t ldx, const Force& f, hipStream_t s) {
   switch (batch) {
-    case 1: return launch3<LAYOUT, XT, 1, NP>(parts, count, nb, x, ldx, s);
-    case 2: return launch3<LAYOUT, XT, 2, NP>(parts, count, nb, x, ldx, s);
-    case 3: return launch3<LAYOUT, XT, 3, NP>(parts, count, nb, x, ldx, s);
-    case 4: return launch3<LAYOUT, XT, 4, NP>(parts, count, nb, x, ldx, s);
-    case 5: return launch3<LAYOUT, XT, 5, NP>(parts, count, nb, x, ldx, s);
-    case 6: return launch3<LAYOUT, XT, 6, NP>(parts, count, nb, x, ldx, s);
-    case 7: return launch3<LAYOUT, XT, 7, NP>(parts, count, nb, x, ldx, s);
-    default: return launch3<LAYOUT, XT, 8, NP>(parts, count, nb, x, ldx, s);
+    case 1: return launch3<LAYOUT, XT, 1, NP>(parts, count, nb, x, ldx, f, s);
+    case 2: return launch3<LAYOUT, XT, 2, NP>(parts, count, nb, x, ldx, f, s);
+    case 3: return launch3<LAYOUT, XT, 3, NP>(parts, count, nb, x, ldx, f, s);
+    case 4: return launch3<LAYOUT, XT, 4, NP>(parts, count, nb, x, ldx, f, s);
+    case 5: return launch3<LAYOUT, XT, 5, NP>(parts, count, nb, x, ldx, f, s);
+    case 6: return launch3<LAYOUT, XT, 6, NP>(parts, count, nb, x, ldx, f, s);
+    case 7: return launch3<LAYOUT, XT, 7, NP>(parts, count, nb, x, ldx, f, s);
+    default: return launch3<LAYOUT, XT, 8, NP>(parts, count, nb, x, ldx, f, s);
   }
 }
 
 // Entry for one activation dtype (each dtype is compiled in its own translation unit).
 template <int XT>
 hipError_t launch_gemv_xt(const GemvPart* parts, int count, int layout, int nb, const uint16_t* x,
-                          int batch, int64_t ldx, hipStream_t s) {
+                          int batch, int64_t ldx, const Force& f, hipStream_t s) {
   if (count == 1)
-    return layout == kDual ? launch2<kDual, XT, 1>(parts, count, nb, x, batch, ldx, s)
-                           : launch2<kFast, XT, 1>(parts, count, nb, x, batch, ldx, s);
-  return layout == kDual ? launch2<kDual, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, s)
-                         : launch2<kFast, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, s);
+    return layout == kDual ? launch2<kDual, XT, 1>(parts, count, nb, x, batch, ldx, f, s)
+                           : launch2<kFast, XT, 1>(parts, count, nb, x, batch, ldx, f, s);
+  return layout == kDual ? launch2<kDual, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, f, s)
+                         : launch2<kFast, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, f, s);
 }
 
 }  // namespace

@@ -303,10 +303,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   if (R == 1 && splits > 1) {
     // Leave this part's sums (tile-major, weight row, batch row), then let the last part
     // to arrive add all parts in part order, so the result does not depend on the
-    // arrival order. The sums and counters are written and read with agent-scope
-    // accesses (coherent across the XCDs' L2 caches without flushing them, as full
-    // release/acquire fences would, which measured 3-5x slower), and the sums are
-    // complete (s_waitcnt) before the arrival is counted.
+    // arrival order.
+    // Ordering. Every access to the sums and counters is an agent-scope atomic, which
+    // gfx950 code carries out at the device's coherence point: the stores write
+    // through (sc1), the loads bypass the non-coherent caches (sc1), the counter is an
+    // atomic read-modify-write. s_waitcnt(0) holds the counter update back until every
+    // store of this wavefront has completed, so a part that counts itself has its sums
+    // in coherent memory; the last part's loads are issued only after its counter
+    // update has returned (its value decides whether they run), so they read every
+    // part's sums. A release on the counter and an acquire after it would compile to the
+    // same instructions plus a write-back and an invalidation of the whole L2
+    // (buffer_wbl2 sc1, buffer_inv sc1), which only matter for data written or read
+    // without sc1 (there is none here) and measured 3-5x slower on these launches.
     float* const mine = partial + (static_cast<int64_t>(part) * tiles + tile) * 128;
     if (lane < 32) {
 #pragma unroll
@@ -360,17 +368,19 @@ struct MfmaPlan {
 // parts, 21.2/23.4/32.3 in four; rows of 5-6 chunks (6144 x 5120, 5120 x 6144, 1024 x
 // 5120) are slower split, since combining the parts adds round trips to memory at the
 // end of a short launch. The partial sums and arrival counters live in a
-// per-(device, stream) workspace: the counters first (a fixed region for up to
-// kMaxSplitTiles tiles, zero at allocation and reset by each launch), then the sums.
-// RFP4_GEMV_SPLIT = "1", "2" or "4", read on each call, forces a split (reduced to at
-// least one chunk per part).
+// per-(device, stream) workspace of fixed size: the counters first (a region for up to
+// kMaxSplitTiles tiles, zero at allocation and reset by the last arrival of each
+// tile), then the sums of up to kMaxSplits parts. A forced split (rfp4_force) is
+// reduced to at least one chunk per part.
 constexpr int kMaxSplitTiles = 1024;
+constexpr int kMaxSplits = 4;
 constexpr size_t kSplitCounterBytes = kMaxSplitTiles * sizeof(int);
-inline int mfma_splits(int tiles, int nu) {
+constexpr size_t kSplitWorkspaceBytes =
+    kSplitCounterBytes + static_cast<size_t>(kMaxSplits) * kMaxSplitTiles * 128 * sizeof(float);
+inline int mfma_splits(int tiles, int nu, const Force& force) {
   const int t_all = (nu + 4 * kMfmaWaves - 1) / (4 * kMfmaWaves);
   int s = (tiles < 4 * device_cu_count() && t_all >= 12) ? 2 : 1;
-  const char* env = getenv("RFP4_GEMV_SPLIT");
-  if (env != nullptr && (env[0] == '1' || env[0] == '2' || env[0] == '4') && env[1] == '\0') s = env[0] - '0';
+  if (force.gemv_splits != 0) s = force.gemv_splits;
   if (tiles > kMaxSplitTiles) s = 1;
   while (s > 1 && t_all < s) s /= 2;
   return s;
@@ -384,7 +394,7 @@ inline size_t mfma_lds(int p, int batch, int r) {
   return 128 * 16 + (chunk > red ? chunk : red);
 }
 
-inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch) {
+inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch, const Force& force) {
   MfmaPlan pl;
   pl.p = nb % 2 == 0 ? 2 : 1;
   pl.nu = nb / pl.p;
@@ -399,7 +409,7 @@ inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch) {
   pl.tiles = 0;
   for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 16 * pl.r - 1) / (16 * pl.r));
   pl.shm = mfma_lds(pl.p, batch, pl.r);
-  pl.splits = pl.r == 1 ? mfma_splits(pl.tiles, pl.nu) : 1;
+  pl.splits = pl.r == 1 ? mfma_splits(pl.tiles, pl.nu, force) : 1;
   return pl;
 }
 
@@ -418,14 +428,14 @@ hipError_t launch_mfma_p(const MfmaPlan& pl, const GemvParts<NP>& gp, const uint
 
 template <int LAYOUT, int XT, int NP>
 hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t* x, int batch,
-                       int64_t ldx, hipStream_t stream) {
-  MfmaPlan pl = mfma_plan(parts, count, nb, batch);
+                       int64_t ldx, const Force& force, hipStream_t stream) {
+  MfmaPlan pl = mfma_plan(parts, count, nb, batch, force);
   float* partial = nullptr;
   int* arrivals = nullptr;
   if (pl.splits > 1) {
-    const size_t bytes = kSplitCounterBytes + static_cast<size_t>(pl.splits) * pl.tiles * 128 * sizeof(float);
+    // Always the fixed maximum, so the workspace is allocated once and never replaced.
     void* ws = nullptr;
-    if (stream_workspace(kWorkspaceGemv, stream, bytes, &ws) != hipSuccess) {
+    if (stream_workspace(kWorkspaceGemv, stream, kSplitWorkspaceBytes, true, &ws) != hipSuccess) {
       pl.splits = 1;  // no workspace (first call under graph capture, or no memory): no split
     } else {
       arrivals = static_cast<int*>(ws);
@@ -458,16 +468,11 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
 // q + k + v (9.75 / 10.15 with the dot-product kernel) or fused gate + up, 34816 rows
 // (28.0 / 29.9), where the matrix-core tiles fill the CUs evenly; from batch 3 the
 // matrix cores win on all of these (their decode does not grow with the batch).
-// The environment variable RFP4_GEMV_MFMA = "0" selects the dot-product kernel and "1"
-// the matrix cores for every launch.
-#ifndef RFP4_GEMV_MFMA_MIN_BATCH
-#define RFP4_GEMV_MFMA_MIN_BATCH 2
-#endif
-inline bool use_mfma(const GemvPart* parts, int count, int nb, int batch) {
-  const char* env = getenv("RFP4_GEMV_MFMA");
-  if (env != nullptr && env[0] == '0') return false;
-  if (env != nullptr && env[0] == '1') return true;
-  if (batch < RFP4_GEMV_MFMA_MIN_BATCH) return false;
+// A forced kernel (rfp4_force) replaces the choice.
+inline bool use_mfma(const GemvPart* parts, int count, int nb, int batch, const Force& force) {
+  if (force.gemv_kernel == RFP4_GEMV_KERNEL_DOT) return false;
+  if (force.gemv_kernel == RFP4_GEMV_KERNEL_TILES) return true;
+  if (batch < 2) return false;
   if (batch == 2) {
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += parts[i].n;
@@ -478,12 +483,12 @@ inline bool use_mfma(const GemvPart* parts, int count, int nb, int batch) {
 
 template <int XT>
 hipError_t launch_gemv_mfma_xt(const GemvPart* parts, int count, int layout, int nb, const uint16_t* x,
-                               int batch, int64_t ldx, hipStream_t s) {
+                               int batch, int64_t ldx, const Force& f, hipStream_t s) {
   if (count == 1)
-    return layout == kDual ? launch_mfma<kDual, XT, 1>(parts, count, nb, x, batch, ldx, s)
-                           : launch_mfma<kFast, XT, 1>(parts, count, nb, x, batch, ldx, s);
-  return layout == kDual ? launch_mfma<kDual, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, s)
-                         : launch_mfma<kFast, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, s);
+    return layout == kDual ? launch_mfma<kDual, XT, 1>(parts, count, nb, x, batch, ldx, f, s)
+                           : launch_mfma<kFast, XT, 1>(parts, count, nb, x, batch, ldx, f, s);
+  return layout == kDual ? launch_mfma<kDual, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, f, s)
+                         : launch_mfma<kFast, XT, kMaxGemvParts>(parts, count, nb, x, batch, ldx, f, s);
 }
 
 }  // namespace

@@ -32,8 +32,6 @@
 
 #pragma once
 
-#include <stdlib.h>
-
 #include "rfp4_internal.h"
 
 namespace rfp4 {
@@ -165,14 +163,15 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
   if (wv == 0 && g == 0) parts.y[mi][row] = 0.5f * (((red[0][nl] + red[1][nl]) + red[2][nl]) + red[3][nl]);
 }
 
-// Whether a batch-1 launch takes the tall kernel. RFP4_GEMV_TALL = 0 / 1 turns it off /
-// on wherever the shape allows (tests); RFP4_GEMV_MFMA = 0 (the dot-product kernel
-// forced) turns it off. By default, from timings against the dot-product kernel on one
-// machine: k = 5120 only (at k = 6144 it was 7-10 % slower from 12288 rows), at least
-// two tiles per CU, and the busiest CU at most 7 % above the average tile count (at
-// 17408 rows, 4.25 tiles per CU, it was 2-5 % slower; with even tile counts from 2 to
-// 8.5 per CU it tied or won by up to 9 %).
-inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb, int batch) {
+// Whether a batch-1 launch takes the tall kernel. A forced kernel (rfp4_force) turns it
+// off (dot product, tiles, no-tall) or on wherever the shape allows (tall). By default,
+// from timings against the dot-product kernel on one machine: k = 5120 only (at k =
+// 6144 it was 7-10 % slower from 12288 rows), at least two tiles per CU, and the
+// busiest CU at most 7 % above the average tile count (at 17408 rows, 4.25 tiles per
+// CU, it was 2-5 % slower; with even tile counts from 2 to 8.5 per CU it tied or won
+// by up to 9 %).
+inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb, int batch,
+                           const Force& force) {
   if (layout != kDual || batch != 1 || (nb != 160 && nb != 192)) return false;
   int64_t tiles = 0;
   for (int i = 0; i < count; ++i) {
@@ -180,11 +179,9 @@ inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb,
     tiles += parts[i].n / 16;
   }
   if (tiles >= (int64_t(1) << 31)) return false;
-  const char* env = getenv("RFP4_GEMV_TALL");
-  if (env != nullptr && env[0] == '0') return false;
-  const char* mf = getenv("RFP4_GEMV_MFMA");
-  if (mf != nullptr && mf[0] == '0') return false;
-  if (env != nullptr && env[0] == '1') return true;
+  const int fk = force.gemv_kernel;
+  if (fk == RFP4_GEMV_KERNEL_DOT || fk == RFP4_GEMV_KERNEL_TILES || fk == RFP4_GEMV_KERNEL_NO_TALL) return false;
+  if (fk == RFP4_GEMV_KERNEL_TALL) return true;
   if (nb != 160) return false;
   const int64_t cus = device_cu_count();
   const int64_t busiest = (tiles + cus - 1) / cus;

@@ -36,6 +36,27 @@ rfp4_status check_weights(const void* w, int layout, int64_t n, int64_t k) {
 
 rfp4_status from_hip(hipError_t e) { return e == hipSuccess ? RFP4_OK : RFP4_ERR_HIP; }
 
+// Copies `force` (NULL = all defaults) after checking every field against the values
+// rfp4.h lists.
+rfp4_status check_force(const rfp4_force* force, rfp4::Force* out) {
+  *out = rfp4::Force{};
+  if (force == nullptr) return RFP4_OK;
+  const rfp4_force& f = *force;
+  if (f.gemv_kernel < RFP4_GEMV_KERNEL_AUTO || f.gemv_kernel > RFP4_GEMV_KERNEL_NO_TALL) return RFP4_ERR_UNSUPPORTED;
+  if (f.gemv_unit_blocks == 0) {
+    if (f.gemv_lanes_per_row != 0) return RFP4_ERR_UNSUPPORTED;
+  } else {
+    const int cl = f.gemv_lanes_per_row;
+    if (f.gemv_unit_blocks != 1 && f.gemv_unit_blocks != 2) return RFP4_ERR_UNSUPPORTED;
+    if (cl < 1 || cl > 64 || (cl & (cl - 1)) != 0) return RFP4_ERR_UNSUPPORTED;
+  }
+  if (f.gemv_splits != 0 && f.gemv_splits != 1 && f.gemv_splits != 2 && f.gemv_splits != 4)
+    return RFP4_ERR_UNSUPPORTED;
+  if (f.gemm_plan < RFP4_GEMM_PLAN_AUTO || f.gemm_plan > RFP4_GEMM_PLAN_NOSPLIT) return RFP4_ERR_UNSUPPORTED;
+  *out = f;
+  return RFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,9 +114,12 @@ rfp4_status rfp4_dequant(const void* w, int layout, int64_t n, int64_t k, float*
                                        static_cast<hipStream_t>(stream)));
 }
 
-rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int64_t* n, int layout,
-                            int64_t k, const void* x, int xdtype, int64_t batch, int64_t ldx,
-                            float* const* y, const int64_t* ldy, void* stream) {
+rfp4_status rfp4_gemv_multi_ex(int count, const void* const* w, const int64_t* n, int layout,
+                               int64_t k, const void* x, int xdtype, int64_t batch, int64_t ldx,
+                               float* const* y, const int64_t* ldy, const rfp4_force* force,
+                               void* stream) {
+  rfp4::Force f;
+  if (check_force(force, &f) != RFP4_OK) return RFP4_ERR_UNSUPPORTED;
   if (count < 1 || count > RFP4_MAX_GEMV_PARTS) return RFP4_ERR_SHAPE;
   if (w == nullptr || n == nullptr || y == nullptr || ldy == nullptr) return RFP4_ERR_NULL;
   rfp4::GemvPart parts[rfp4::kMaxGemvParts];
@@ -116,13 +140,19 @@ rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int64_t* n, i
   if (x == nullptr) return RFP4_ERR_NULL;
   if (!aligned16(x) || (ldx % 8) != 0) return RFP4_ERR_UNSUPPORTED;
   return from_hip(rfp4::launch_gemv(parts, count, layout, k, x, xdtype, static_cast<int>(batch),
-                                    ldx, static_cast<hipStream_t>(stream)));
+                                    ldx, f, static_cast<hipStream_t>(stream)));
+}
+
+rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int64_t* n, int layout,
+                            int64_t k, const void* x, int xdtype, int64_t batch, int64_t ldx,
+                            float* const* y, const int64_t* ldy, void* stream) {
+  return rfp4_gemv_multi_ex(count, w, n, layout, k, x, xdtype, batch, ldx, y, ldy, nullptr, stream);
 }
 
 rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const void* x,
                       int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,
                       void* stream) {
-  return rfp4_gemv_multi(1, &w, &n, layout, k, x, xdtype, batch, ldx, &y, &ldy, stream);
+  return rfp4_gemv_multi_ex(1, &w, &n, layout, k, x, xdtype, batch, ldx, &y, &ldy, nullptr, stream);
 }
 
 rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int64_t k, uint16_t* out,
@@ -167,14 +197,22 @@ rfp4_status rfp4_gemm_dequant(const void* w, int layout, int64_t n, int64_t k, c
                                                         m, lda, static_cast<uint16_t*>(c), ldc, s));
 }
 
-rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
-                      int64_t m, int64_t lda, void* c, int64_t ldc, void* stream) {
+rfp4_status rfp4_gemm_ex(const void* w, int layout, int64_t n, int64_t k, const void* a,
+                         int64_t m, int64_t lda, void* c, int64_t ldc, const rfp4_force* force,
+                         void* stream) {
+  rfp4::Force f;
+  if (check_force(force, &f) != RFP4_OK) return RFP4_ERR_UNSUPPORTED;
   rfp4_status st = check_gemm(w, layout, n, k, a, m, lda, c, ldc);
   if (st != RFP4_OK) return st;
   return from_hip(rfp4::launch_gemm(static_cast<const uint8_t*>(w), layout, n, k,
                                     static_cast<const uint16_t*>(a), m, lda,
-                                    static_cast<uint16_t*>(c), ldc,
+                                    static_cast<uint16_t*>(c), ldc, f,
                                     static_cast<hipStream_t>(stream)));
+}
+
+rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
+                      int64_t m, int64_t lda, void* c, int64_t ldc, void* stream) {
+  return rfp4_gemm_ex(w, layout, n, k, a, m, lda, c, ldc, nullptr, stream);
 }
 
 rfp4_status rfp4_quantize(const void* src, int src_dtype, int64_t n, int64_t k, int64_t lds,

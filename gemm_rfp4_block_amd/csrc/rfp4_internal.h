@@ -7,6 +7,8 @@
 
 #include <atomic>
 
+#include "rfp4.h"
+
 namespace rfp4 {
 
 constexpr int kDual = 0;
@@ -21,12 +23,20 @@ constexpr int block_bytes(int layout) { return layout == kDual ? 18 : 17; }
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
-// Per-(kind, device, stream) device workspace of at least `bytes`, zero-filled when
-// (re)allocated, kept until the process ends; hipErrorStreamCaptureUnsupported while
-// the stream is being captured and the workspace is too small.
+// Per-(kind, device, stream) device workspace of at least `bytes`, kept until the
+// process ends. A workspace is never freed and nothing synchronizes: when a launch needs
+// more than the stream has, a new buffer of at least twice the old size is allocated
+// and the old one is kept, unused (a graph captured earlier may still write to it).
+// A new buffer is zero-filled (an asynchronous fill ordered on the stream) when
+// `zero` is set. hipErrorStreamCaptureUnsupported while the stream is being captured
+// and its workspace is too small (nothing is allocated during a capture).
 constexpr int kWorkspaceGemm = 0;  // k-split partial tiles of rfp4_gemm
 constexpr int kWorkspaceGemv = 1;  // split-chunk partial sums and arrival counters of rfp4_gemv
-hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void** out);
+hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, bool zero, void** out);
+
+// The kernel and plan overrides of the _ex entry points (rfp4_force in rfp4.h), checked
+// by the API layer; a zero-filled struct is the default behaviour.
+typedef rfp4_force Force;
 
 // Launchers. Arguments have been checked by the API layer: shapes in range, rows
 // 16-byte aligned, pointers non-null and aligned as the public header requires.
@@ -55,14 +65,15 @@ struct GemvPart {
 
 // 1 <= count <= kMaxGemvParts matrices sharing k and the activations.
 hipError_t launch_gemv(const GemvPart* parts, int count, int layout, int64_t k, const void* x,
-                       int xdtype, int batch, int64_t ldx, hipStream_t stream);
+                       int xdtype, int batch, int64_t ldx, const Force& force, hipStream_t stream);
 // The same for one activation dtype (nb = k / 32 blocks per row).
 hipError_t launch_gemv_f16(const GemvPart* parts, int count, int layout, int nb, const uint16_t* x,
-                           int batch, int64_t ldx, hipStream_t stream);
+                           int batch, int64_t ldx, const Force& force, hipStream_t stream);
 hipError_t launch_gemv_bf16(const GemvPart* parts, int count, int layout, int nb, const uint16_t* x,
-                            int batch, int64_t ldx, hipStream_t stream);
+                            int batch, int64_t ldx, const Force& force, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
-                       int64_t m, int64_t lda, uint16_t* c, int64_t ldc, hipStream_t stream);
+                       int64_t m, int64_t lda, uint16_t* c, int64_t ldc, const Force& force,
+                       hipStream_t stream);
 
 }  // namespace rfp4

@@ -23,12 +23,14 @@
  *
  * General rules for every entry point:
  *   - All pointers except rfp4_validate's `w_host` are device pointers. The caller
- *     owns every buffer it passes. The dequant and encoder entry points never
- *     allocate, free or synchronize; rfp4_gemm and rfp4_gemv(_multi) may use a
- *     workspace of their own (see there) and rfp4_gemm_dequant uses rocBLAS. Global
- *     state: per-device caches of the CU count and of kernel attributes (atomics),
- *     the workspaces and the rocBLAS handles (behind mutexes), so calls from several
- *     threads are safe.
+ *     owns every buffer it passes. No entry point frees memory or synchronizes a
+ *     stream or the device. The dequant, encoder and validation entry points never
+ *     allocate; rfp4_gemm and rfp4_gemv(_multi) allocate a workspace at its first need
+ *     (see there) and keep it; rfp4_gemm_dequant uses rocBLAS, which keeps handles and
+ *     workspace of its own. Global state: per-device caches of the CU count and of
+ *     kernel attributes (atomics), the workspaces and the rocBLAS handles (behind
+ *     mutexes), so calls from several threads are safe. Nothing reads the
+ *     environment.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are
  *     asynchronous and ordered on that stream; a fault in a kernel surfaces at the
  *     caller's next synchronization.
@@ -38,7 +40,9 @@
  *   - Alignment: W must start on a 16-byte boundary (RFP4_ERR_UNSUPPORTED
  *     otherwise); its rows may have any length, so k is any multiple of 32 and rows
  *     need not start on a 16-byte boundary. Activations and outputs must be 16-byte
- *     aligned with leading dimensions that keep every row 16-byte aligned.
+ *     aligned with leading dimensions that keep every row 16-byte aligned (every
+ *     activation and output row is moved with 16-byte vector accesses; buffers from
+ *     a device allocator meet this, slices at odd offsets do not).
  *   - Sizes: 1 <= n, m and 32 <= k, with n, m, k <= 2^31 - 1 and W at most 2^40
  *     bytes (RFP4_ERR_SHAPE otherwise); buffers are addressed with 64-bit offsets.
  */
@@ -115,28 +119,27 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * Options", Option 2): for b < batch and r < n,
  *   y[b * ldy + r] = sum_c weight(r, c) * x[b * ldx + c]
  * with x of dtype xdtype (RFP4_F16 or RFP4_BF16), products formed exactly and summed
- * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n. Batch 1 runs a
- * dot-product kernel, batches from 3 on a matrix-core kernel, batch 2 the dot-product
- * kernel when k >= 6144 or the launch has >= 16384 rows in all, and fewer than 32768
- * rows, the matrix-core kernel otherwise (the summation order, hence the last bits, differ between the
- * two); the environment variable
- * RFP4_GEMV_MFMA = "0" or "1", read on each call, forces one of them. Batch-1 launches
- * with the dual layout, f16 activations, k = 5120 and every matrix's rows a multiple of
- * 16, of at least two 16-row tiles per CU spread evenly over the CUs (the busiest at
- * most 7 % above the average), run a third, matrix-core kernel (again other last
- * bits); RFP4_GEMV_TALL = "0" or "1" turns it off, or on wherever the shape allows
- * (k = 5120 or 6144), and RFP4_GEMV_MFMA = "0" turns it off. On long rows
- * (at least 12 chunks of 16 units, a unit being two blocks when k / 32 is even and one
- * otherwise: k >= 11328 or k >= 5664) with fewer than four 16-row tiles per CU the
- * matrix-core kernel gives
- * each tile's k range to two workgroups whose fp32 partial sums meet in a small
- * device workspace (under 1 MB) that the library allocates per (device, stream) on
- * first need and keeps; the parts are added in a fixed order, so results are
- * deterministic. It is never allocated during graph capture (the launch then runs
- * unsplit, which changes the last bits), so call once before capturing. A captured
- * split launch keeps using the capturing stream's workspace: replay such a graph only
- * ordered with that stream's other work and with its own other replays.
- * RFP4_GEMV_SPLIT = "1", "2" or "4" forces the number of parts. */
+ * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n.
+ * Kernel choice (each sums in its own fp32 order, so the last bits differ between
+ * them; rfp4_gemv_multi_ex can force one):
+ *   - batch 1: a dot-product kernel; launches with the dual layout, f16 activations,
+ *     k = 5120, every matrix's rows a multiple of 16 and at least two 16-row tiles per
+ *     CU spread evenly over the CUs (the busiest at most 7 % above the average) run a
+ *     batch-1 matrix-core kernel ("tall") instead;
+ *   - batch 2: the dot-product kernel when k >= 6144 or the launch has >= 16384 rows
+ *     in all, and fewer than 32768 rows; otherwise, like every batch from 3 on, a
+ *     matrix-core kernel of 16-row tiles.
+ * Workspace: on long rows (at least 12 chunks of 16 units, a unit being two blocks
+ * when k / 32 is even and one otherwise) with fewer than four 16-row tiles per CU the
+ * tile kernel gives each tile's k range to two workgroups whose fp32 partial sums
+ * meet in a device workspace of fixed size (2 MiB + 4 KiB) that the library
+ * allocates once per (device, stream) at its first need and keeps until the process
+ * ends; the parts are added in a fixed order, so results are deterministic. The
+ * workspace is never freed or reallocated, and no call synchronizes. It is never
+ * allocated while the stream is being captured into a graph (the launch then runs
+ * unsplit, which changes the last bits), so call once on a stream before capturing on
+ * it. A captured split launch uses the capturing stream's workspace: replay such a
+ * graph only ordered with that stream's other work and with its own other replays. */
 RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, const void* x,
                       int xdtype, int64_t batch, int64_t ldx, float* y, int64_t ldy,
                       void* stream);
@@ -145,13 +148,13 @@ RFP4_API rfp4_status rfp4_gemv(const void* w, int layout, int64_t n, int64_t k, 
  * gemv_gate_up ("Kernel System"), also used for q/k/v. For i < count, part i computes
  *   y[i][b * ldy[i] + r] = sum_c weight_i(r, c) * x[b * ldx + c],  r < n[i], b < batch
  * as rfp4_gemv does for w[i], with the same layout and k for every part and the same
- * accuracy (the lane mapping, and so the fp32 summation order, is chosen for the launch
- * as a whole; with the same mapping the results equal separate rfp4_gemv calls bit for
- * bit). The row groups of all parts are split evenly over the CUs, so small matrices
- * (k/v) ride along with large ones. `w`, `n`, `y` and `ldy` are host arrays of
- * `count` entries (1 <= count <= RFP4_MAX_GEMV_PARTS) holding device pointers and
- * sizes; the total row count must be <= 2^31 - 1. Every part is checked as in
- * rfp4_gemv before any HIP call. */
+ * accuracy (the kernel and lane mapping, and so the fp32 summation order, are chosen
+ * for the launch as a whole; with the same mapping the results equal separate
+ * rfp4_gemv calls bit for bit). The row groups of all parts are split evenly over the
+ * CUs, so small matrices (k/v) ride along with large ones. `w`, `n`, `y` and `ldy` are
+ * host arrays of `count` entries (1 <= count <= RFP4_MAX_GEMV_PARTS) holding device
+ * pointers and sizes; the total row count must be <= 2^31 - 1. Every part is checked
+ * as in rfp4_gemv before any HIP call. Workspace as rfp4_gemv. */
 #define RFP4_MAX_GEMV_PARTS 8
 RFP4_API rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int64_t* n,
                                      int layout, int64_t k, const void* x, int xdtype,
@@ -166,21 +169,71 @@ RFP4_API rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int6
  * m * lda, m * ldc <= 2^39 (RFP4_ERR_SHAPE otherwise).
  * Balance: the columns of C are split between 256 x 256 tiles and trailing strips of
  * 128 x 128 tiles, and the k range of either kind of tile may be split in two or more
- * parts, as a cost model of the launch picks. Split tiles write fp32 partial sums to a
- * device workspace that the
- * library allocates per (device, stream) on first need, grows when a larger one is
- * needed (synchronizing that stream first) and keeps until the process ends; a
- * final kernel adds the parts in a fixed order and rounds to bf16. The workspace is
- * never allocated while the stream is being captured into a graph (the split is
- * then skipped), so call once before capturing; a captured split launch keeps using
- * the capturing stream's workspace, so replay such a graph only ordered with that
- * stream's other work and with its own other replays. Results are deterministic for a
- * given shape and CU count. The environment variable RFP4_GEMM_PLAN, read on each
- * call, forces a plan: "main" (256 x 256 tiles only), "msplit2", "msplit3", "msplit4"
- * (256 x 256 tiles only, k split 2, 3 or 4 ways), "tail", "tail2", "tail4" (128 x 128
- * tiles only, k unsplit or split 2 or 4 ways), "nosplit" (no k split). */
+ * parts, as a cost model of the launch picks (at most 512 MiB of partial sums). Split
+ * tiles write fp32 partial sums to a device workspace that the library allocates per
+ * (device, stream) at the first need and enlarges (at least doubling) when a launch
+ * needs more; a final kernel adds the parts in a fixed order and rounds to bf16.
+ * Nothing is ever freed or synchronized: an outgrown workspace is kept, unused, until
+ * the process ends, so a graph captured earlier still owns valid memory. No workspace
+ * is allocated or enlarged while the stream is being captured (the split is then
+ * skipped, which changes the last bits), so call once with the largest shape before
+ * capturing; a captured split launch uses the workspace the capturing stream had,
+ * so replay such a graph only ordered with that stream's other work and with its own
+ * other replays. Results are deterministic for a given shape and CU count. */
 RFP4_API rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,
                       int64_t m, int64_t lda, void* c, int64_t ldc, void* stream);
+
+/* Forcing a kernel or plan (tests and experiments). The default entry points choose
+ * every kernel, lane mapping, split and tiling themselves; the _ex variants below take
+ * an rfp4_force that overrides some of those choices. NULL, or a zero-filled struct,
+ * gives exactly the default entry point's behaviour. Forcing changes only which
+ * kernel runs and in which fp32 summation order, never what is computed. A field
+ * outside its listed values gives RFP4_ERR_UNSUPPORTED before any HIP call. */
+typedef enum rfp4_gemv_kernel {
+  RFP4_GEMV_KERNEL_AUTO = 0,    /* the default choice */
+  RFP4_GEMV_KERNEL_DOT = 1,     /* the dot-product kernel, at every batch */
+  RFP4_GEMV_KERNEL_TILES = 2,   /* the matrix-core kernel of 16-row tiles, at every batch */
+  RFP4_GEMV_KERNEL_TALL = 3,    /* the batch-1 tall matrix-core kernel wherever its shape
+                                   rules allow (dual, f16, batch 1, k = 5120 or 6144, every
+                                   matrix's rows a multiple of 16), else the default */
+  RFP4_GEMV_KERNEL_NO_TALL = 4  /* the default choice without the tall kernel */
+} rfp4_gemv_kernel;
+
+typedef enum rfp4_gemm_plan {
+  RFP4_GEMM_PLAN_AUTO = 0,     /* the cost model's choice */
+  RFP4_GEMM_PLAN_MAIN = 1,     /* 256 x 256 tiles only, k unsplit */
+  RFP4_GEMM_PLAN_MSPLIT2 = 2,  /* 256 x 256 tiles only, k split 2, 3 or 4 ways (fewer */
+  RFP4_GEMM_PLAN_MSPLIT3 = 3,  /*   where k has too few 128-column steps) */
+  RFP4_GEMM_PLAN_MSPLIT4 = 4,
+  RFP4_GEMM_PLAN_TAIL = 5,     /* 128 x 128 tiles only, k unsplit, split 2 or 4 ways */
+  RFP4_GEMM_PLAN_TAIL2 = 6,
+  RFP4_GEMM_PLAN_TAIL4 = 7,
+  RFP4_GEMM_PLAN_NOSPLIT = 8   /* the cost model's choice among plans without a k split */
+} rfp4_gemm_plan;
+
+typedef struct rfp4_force {
+  int32_t gemv_kernel;         /* rfp4_gemv_kernel */
+  int32_t gemv_unit_blocks;    /* dot-product kernel: consecutive blocks per lane unit, 1
+                                  or 2, together with gemv_lanes_per_row; 0 = the default
+                                  mapping (a pair mapping on an odd k / 32 is ignored) */
+  int32_t gemv_lanes_per_row;  /* dot-product kernel: lanes per weight row, a power of two
+                                  from 1 to 64 (0 with gemv_unit_blocks = 0) */
+  int32_t gemv_splits;         /* tile kernel: parts of each tile's k range, 1, 2 or 4
+                                  (fewer where a row has fewer chunks); 0 = default */
+  int32_t gemm_plan;           /* rfp4_gemm_plan */
+} rfp4_force;
+
+/* rfp4_gemv_multi with `force` (may be NULL); rfp4_gemv is count = 1. */
+RFP4_API rfp4_status rfp4_gemv_multi_ex(int count, const void* const* w, const int64_t* n,
+                                        int layout, int64_t k, const void* x, int xdtype,
+                                        int64_t batch, int64_t ldx, float* const* y,
+                                        const int64_t* ldy, const rfp4_force* force,
+                                        void* stream);
+
+/* rfp4_gemm with `force` (may be NULL). */
+RFP4_API rfp4_status rfp4_gemm_ex(const void* w, int layout, int64_t n, int64_t k, const void* a,
+                                  int64_t m, int64_t lda, void* c, int64_t ldc,
+                                  const rfp4_force* force, void* stream);
 
 /* Dequantize-then-multiply prefill, the comparison baseline of rfp4_gemm ("Kernel
  * System" lists dequantize + dense GEMM beside the fused w4a16_gemm): W is expanded

@@ -9,7 +9,10 @@ Recipe (every workload, seed fixed per workload):
 
 * index bytes: uniform 0..255, so both 4-bit indices of a byte are uniform 0..15;
 * scale bytes: (E << 3) | M with exponent field E uniform in 4..9 and mantissa M
-  uniform in 0..7, bit 7 clear (finite, unsigned E4M3);
+  uniform in 0..7, bit 7 clear (finite, unsigned E4M3); or, for the scale-range
+  tests, uniform over all 254 finite bytes (every byte but 0x7F and 0xFF: bit 7 set
+  or clear, exponent field 0 included), with the first 254 scale bytes of each half
+  running through all of them in a seeded random order;
 * stress blocks (down-projection workload): a fraction of the blocks, drawn without
   replacement, get every index in {7, 15} (magnitude 10, random sign) and scale
   (15 << 3) | M with M uniform in 0..6 (the largest finite exponent);
@@ -42,15 +45,28 @@ def row_bytes(layout: int, k: int) -> int:
     return (k // 32) * _BLOCK_BYTES[layout]
 
 
+# The 254 byte values a validated row may hold as a scale byte ("Scale Format": the
+# bytes whose low seven bits are all ones are the non-finite ones).
+FINITE_SCALE_BYTES = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+
+
 def weights(rng: np.random.Generator, layout: int, n: int, k: int,
-            stress_frac: float = 0.0, exp_lo: int = 4, exp_hi: int = 9) -> np.ndarray:
-    """Packed weight bytes, uint8 array of shape (n, row_bytes)."""
+            stress_frac: float = 0.0, exp_lo: int = 4, exp_hi: int = 9,
+            all_scales: bool = False) -> np.ndarray:
+    """Packed weight bytes, uint8 array of shape (n, row_bytes). With all_scales, the
+    scale bytes are drawn from every finite byte (see the module recipe)."""
     nb = k // 32
     ns = _SCALES[layout]
     qs = rng.integers(0, 256, size=(n, nb, 16), dtype=np.uint8)
-    ex = rng.integers(exp_lo, exp_hi + 1, size=(n, nb, ns), dtype=np.uint8)
-    mu = rng.integers(0, 8, size=(n, nb, ns), dtype=np.uint8)
-    sc = (ex << 3) | mu
+    if all_scales:
+        sc = FINITE_SCALE_BYTES[rng.integers(0, FINITE_SCALE_BYTES.size, size=(n, nb, ns))]
+        first = min(n * nb, FINITE_SCALE_BYTES.size)
+        for h in range(ns):
+            sc.reshape(n * nb, ns)[:first, h] = rng.permutation(FINITE_SCALE_BYTES)[:first]
+    else:
+        ex = rng.integers(exp_lo, exp_hi + 1, size=(n, nb, ns), dtype=np.uint8)
+        mu = rng.integers(0, 8, size=(n, nb, ns), dtype=np.uint8)
+        sc = (ex << 3) | mu
     if stress_frac > 0.0:
         total = n * nb
         cnt = int(np.floor(stress_frac * total))

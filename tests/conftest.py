@@ -29,3 +29,18 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def force(monkeypatch):
+    """force(**names) -> rfp4_force: the binding's GEMV and GEMM calls take these kernel /
+    plan overrides (gemm_rfp4_block_amd.make_force) for the rest of the test."""
+    import gemm_rfp4_block_amd as R
+    from tests.abi_calls import patch_binding
+
+    def apply(**kw):
+        f = R.make_force(**kw)
+        patch_binding(monkeypatch, f)
+        return f
+
+    return apply

@@ -190,6 +190,52 @@ def test_gemm_argument_errors(L):
     assert f(P, 0, 64, 96, P2, 16, 95, P, 64, NULL) == R.RFP4_ERR_SHAPE  # lda < k, 54-byte rows
 
 
+BAD_FORCES = [  # each field outside the values include/rfp4.h lists
+    dict(gemv_kernel=5), dict(gemv_kernel=-1), dict(gemv_unit_blocks=3, gemv_lanes_per_row=16),
+    dict(gemv_unit_blocks=1, gemv_lanes_per_row=12), dict(gemv_unit_blocks=2, gemv_lanes_per_row=128),
+    dict(gemv_unit_blocks=1, gemv_lanes_per_row=0), dict(gemv_unit_blocks=0, gemv_lanes_per_row=8),
+    dict(gemv_splits=3), dict(gemv_splits=-1), dict(gemm_plan=9), dict(gemm_plan=-2),
+]
+
+
+@pytest.mark.parametrize("bad", BAD_FORCES, ids=lambda d: "-".join(f"{k}{v}" for k, v in d.items()))
+def test_force_fields_checked_before_any_hip_call(L, bad):
+    f = R.Force(**bad)
+    one = (ctypes.c_void_p * 1)(0x10000)
+    n1 = (ctypes.c_int64 * 1)(8)
+    y1 = (ctypes.c_void_p * 1)(0x20000)
+    ld = (ctypes.c_int64 * 1)(8)
+    assert L.rfp4_gemv_multi_ex(1, one, n1, 0, 512, P2, 0, 1, 512, y1, ld, ctypes.byref(f), NULL) == \
+        R.RFP4_ERR_UNSUPPORTED
+    assert L.rfp4_gemm_ex(P, 0, 64, 512, P2, 16, 512, P, 64, ctypes.byref(f), NULL) == R.RFP4_ERR_UNSUPPORTED
+
+
+def test_force_entry_points_check_shapes(L):
+    """A valid (or NULL) force leaves the ordinary argument checks in place."""
+    f = R.make_force("tiles", gemv_splits=2, gemm_plan="tail4")
+    one = (ctypes.c_void_p * 1)(0x10000)
+    n1 = (ctypes.c_int64 * 1)(8)
+    y1 = (ctypes.c_void_p * 1)(0x20000)
+    ld = (ctypes.c_int64 * 1)(8)
+    for fp in (ctypes.byref(f), None):
+        assert L.rfp4_gemv_multi_ex(1, one, n1, 0, 512, P2, 0, 9, 512, y1, ld, fp, NULL) == R.RFP4_ERR_SHAPE
+        assert L.rfp4_gemv_multi_ex(1, one, n1, 0, 512, NULL, 0, 1, 512, y1, ld, fp, NULL) == R.RFP4_ERR_NULL
+        assert L.rfp4_gemm_ex(P, 0, 64, 512, P2, 16, 511, P, 64, fp, NULL) == R.RFP4_ERR_SHAPE
+        assert L.rfp4_gemm_ex(P, 0, 64, 512, P2, 16, 512, UNALIGNED, 64, fp, NULL) == R.RFP4_ERR_UNSUPPORTED
+
+
+def test_library_sources_read_no_environment_and_never_free_or_synchronize():
+    """The product path takes no hidden inputs (no getenv) and never frees memory or
+    synchronizes a stream or the device inside a call."""
+    csrc = os.path.join(ROOT, "gemm_rfp4_block_amd", "csrc")
+    banned = re.compile(r"\b(getenv|secure_getenv|hipFree|hipFreeAsync|hipStreamSynchronize|"
+                        r"hipDeviceSynchronize|hipEventSynchronize)\s*\(")
+    for name in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, name)).read()
+        code = re.sub(r"//[^\n]*", "", text)  # comments may name them
+        assert not banned.search(code), name
+
+
 def test_quantize_argument_errors(L):
     f = L.rfp4_quantize
     assert f(P, 3, 4, 64, 64, 0, P2, NULL) == R.RFP4_ERR_UNSUPPORTED  # dtype

@@ -49,10 +49,10 @@ GEMV_CASES = [
 
 
 @pytest.mark.parametrize("case", GEMV_CASES, ids=lambda c: "L{}n{}k{}b{}{}-s{}".format(*c))
-def test_gemv_repeatable(case, monkeypatch):
+def test_gemv_repeatable(case, force):
     layout, n, k, batch, dt, split = case
     if split is not None:
-        monkeypatch.setenv("RFP4_GEMV_SPLIT", split)
+        force(gemv_splits=int(split))
     w = synth.weights_device(layout, n, k, 11, DEV)
     x = synth.activations_device(batch, k, dt, 12, DEV)
     outs = three_runs(lambda s: R.rfp4_gemv(w, layout, n, k, x, stream=s))
@@ -79,9 +79,9 @@ GEMM_CASES = [
 
 
 @pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: "L{}m{}n{}k{}-{}".format(*c))
-def test_gemm_repeatable(case, monkeypatch):
+def test_gemm_repeatable(case, force):
     layout, m, n, k, plan = case
-    monkeypatch.setenv("RFP4_GEMM_PLAN", plan)
+    force(gemm_plan=plan or "auto")
     w = synth.weights_device(layout, n, k, 31, DEV)
     a = synth.activations_device(m, k, "bf16", 32, DEV)
     outs = three_runs(lambda s: R.rfp4_gemm(w, layout, n, k, a, stream=s))

@@ -33,7 +33,8 @@ def bits(a):
 
 
 def run_gemv(w, layout, n, k, x, ldx=None, ldy=None):
-    """Call rfp4_gemv with optional padded leading dimensions; returns (batch, n) fp32."""
+    """Call rfp4_gemv (through the binding, so the `force` fixture applies) with optional
+    padded leading dimensions; returns (batch, n) fp32."""
     batch = x.shape[0]
     if ldx is None or ldx == k:
         xd = x.to(DEV).contiguous()
@@ -44,10 +45,7 @@ def run_gemv(w, layout, n, k, x, ldx=None, ldy=None):
         xd = buf
     ldy = n if ldy is None else ldy
     y = torch.full((batch, ldy), float("nan"), dtype=torch.float32, device=DEV)
-    wd = dev(w)
-    st = R.lib().rfp4_gemv(R._ptr(wd), layout, n, k, R._ptr(xd), R._xdtype(xd), batch, ldx,
-                           R._ptr(y), ldy, R._stream(None))
-    assert st == R.RFP4_OK, R.rfp4_status_string(st)
+    R.rfp4_gemv(dev(w), layout, n, k, xd, y)  # leading dimensions from the strides
     torch.cuda.synchronize()
     out = y.cpu().numpy()
     if ldy > n:
@@ -222,10 +220,9 @@ GEMV_PLANS = [
 
 
 @pytest.mark.parametrize("case", GEMV_PLANS, ids=lambda c: "{}-L{}n{}k{}b{}{}".format(*c))
-def test_gemv_forced_plan(case, monkeypatch):
+def test_gemv_forced_plan(case, force):
     plan, layout, n, k, batch, dt = case
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")  # lane mappings of the dot-product kernel
-    monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
+    force(gemv_kernel="dot", gemv_plan=tuple(map(int, plan.split(":"))))  # dot-product lane mappings
     rng = np.random.default_rng(5000 + n + k + batch)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
     x = synth.activations(rng, batch, k, dt)
@@ -255,11 +252,10 @@ def test_gemv_multi(case):
         assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
 
 
-def test_gemv_multi_equals_single_calls(monkeypatch):
+def test_gemv_multi_equals_single_calls(force):
     """With the same (forced) lane mapping the fused launch gives exactly the results of
     separate calls."""
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")
-    monkeypatch.setenv("RFP4_GEMV_PLAN", "2:16")
+    force(gemv_kernel="dot", gemv_plan=(2, 16))
     rng = np.random.default_rng(77)
     ns, k = [640, 96, 96], 2048
     ws = [dev(synth.weights(rng, 0, n, k)) for n in ns]
@@ -281,15 +277,14 @@ NONFINITE_X = [  # kernel, plan, layout, n, k, batch, dtype
 
 
 @pytest.mark.parametrize("case", NONFINITE_X, ids=lambda c: "mfma{}-{}-L{}n{}k{}b{}{}".format(*c))
-def test_gemv_nonfinite_activations(case, monkeypatch):
+def test_gemv_nonfinite_activations(case, force):
     """An infinite activation in the last block of a row: rows whose exact sum is +-inf
     (or NaN, where a zero weight meets it) give exactly that; lanes or lane groups past
     the row end, which re-read that last block, must add nothing (not 0 * inf = NaN).
     Other activation rows stay finite and within tolerance."""
     mode, plan, layout, n, k, batch, dt = case
-    monkeypatch.setenv("RFP4_GEMV_MFMA", mode)
-    if plan is not None:
-        monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
+    force(gemv_kernel={"0": "dot", "1": "tiles"}[mode],
+          gemv_plan=tuple(map(int, plan.split(":"))) if plan is not None else None)
     rng = np.random.default_rng(9300 + n + k)
     w = synth.weights(rng, layout, n, k)
     x = synth.activations(rng, batch, k, dt)
@@ -323,12 +318,12 @@ TALL_CASES = [  # row counts of the matrices (one launch), k, activation dtype, 
 
 
 @pytest.mark.parametrize("case", TALL_CASES, ids=lambda c: "n{}k{}{}L{}".format("-".join(map(str, c[0])), *c[1:]))
-def test_gemv_tall_forced(case, monkeypatch):
+def test_gemv_tall_forced(case, force):
     """The batch-1 matrix-core kernel for tall launches, forced on wherever the shape
     allows (RFP4_GEMV_TALL=1), against the oracle; shapes it does not take fall back to
     the dot-product kernel and must stay correct. Weights include 2 % stress blocks
     (extreme codes and scales)."""
-    monkeypatch.setenv("RFP4_GEMV_TALL", "1")
+    force(gemv_kernel="tall")
     ns, k, dt, layout = case
     rng = np.random.default_rng(9900 + sum(ns) + k + layout)
     ws = [synth.weights(rng, layout, n, k, stress_frac=0.02) for n in ns]
@@ -343,11 +338,11 @@ def test_gemv_tall_forced(case, monkeypatch):
         assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
 
 
-def test_gemv_tall_nonfinite_activations(monkeypatch):
+def test_gemv_tall_nonfinite_activations(force):
     """Tall kernel: an infinite activation in the last unit of the rows gives exactly the
     oracle's +-inf or NaN (a zero weight or a zero scale meeting it); the zero-padded A
     rows add nothing."""
-    monkeypatch.setenv("RFP4_GEMV_TALL", "1")
+    force(gemv_kernel="tall")
     layout, n, k = 0, 64, 5120
     rng = np.random.default_rng(9950)
     w = synth.weights(rng, layout, n, k, stress_frac=0.05)
@@ -431,12 +426,12 @@ def test_gemv_extreme_values():
 
 @pytest.mark.parametrize("layout,dt", [(0, "f16"), (1, "bf16")])
 def test_gemv_exact_invariants(layout, dt):
-    """+1 on every scale exponent field doubles y bitwise (the scale enters through an
-    exact fp32 multiply); two runs agree bitwise (fixed reduction order, no atomics).
-    Toggling every index sign negates y to within rounding: the v_dot2_f32_{f16,bf16}
-    instructions that form the partial sums are not correctly rounded and not
-    sign-symmetric (measured on gfx950 against the exactly rounded sum), so an
-    exactly negated input can come back one fp32 ulp away from the negated output."""
+    """The default batch-4 launch (the tile kernel): +1 on every scale exponent field
+    doubles y bitwise (the scale enters through exact operations); two runs agree
+    bitwise (fixed reduction order, no atomics). Toggling every index sign negates y to
+    within rounding: the matrix cores' fp32 accumulation is not sign-symmetric in every
+    case (measured on gfx950, see test_gpu_scale_range.py), so an exactly negated input
+    can come back an fp32 ulp or two away from the negated output."""
     rng = np.random.default_rng(34 + layout)
     n, k = 200, 4096
     w = synth.weights(rng, layout, n, k)
@@ -486,9 +481,7 @@ def run_gemm(w, layout, n, k, a, ldc=None):
     ad = a.to(DEV).contiguous()
     ldc = n if ldc is None else ldc
     c = torch.full((m, ldc), float("nan"), dtype=torch.bfloat16, device=DEV)
-    wd = dev(w)
-    st = R.lib().rfp4_gemm(R._ptr(wd), layout, n, k, R._ptr(ad), m, k, R._ptr(c), ldc, R._stream(None))
-    assert st == R.RFP4_OK, R.rfp4_status_string(st)
+    R.rfp4_gemm(dev(w), layout, n, k, ad, c)  # ldc from the stride; the force fixture applies
     torch.cuda.synchronize()
     out = c.to(torch.float64).cpu().numpy()
     if ldc > n:
@@ -544,9 +537,9 @@ def test_gemm_same_sign_rounding():
 @pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4", "msplit2", "msplit3", "msplit4"])
 @pytest.mark.parametrize("case", [(0, 100, 200, 512), (1, 77, 136, 1024), (0, 257, 520, 2304),
                                   (1, 300, 264, 512)], ids=lambda c: "L{}m{}n{}k{}".format(*c))
-def test_gemm_forced_tile_size(case, plan, monkeypatch):
+def test_gemm_forced_tile_size(case, plan, force):
     """Each tile configuration alone over the whole matrix, ragged edges included."""
-    monkeypatch.setenv("RFP4_GEMM_PLAN", plan)
+    force(gemm_plan=plan)
     layout, m, n, k = case
     rng = np.random.default_rng(4000 + m + n + k)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
@@ -556,7 +549,7 @@ def test_gemm_forced_tile_size(case, plan, monkeypatch):
     assert gemm_error(c, c_ref, den) <= TOL
 
 
-def test_gemm_split_main_tiles_full_size_sampled(monkeypatch):
+def test_gemm_split_main_tiles_full_size_sampled(force):
     """The 2048 x 5120 x 17408 down-projection prefill, for which the planner splits the
     k range of the 256 x 256 tiles three ways; checked on sampled columns."""
     layout, m, n, k = 1, 2048, 5120, 17408
@@ -778,11 +771,10 @@ def test_unaligned_rows_gemv(case):
 @pytest.mark.parametrize("plan", ["1:1", "1:4", "1:64", "2:2", "2:16"])
 @pytest.mark.parametrize("case", [(0, 70, 1408, 2, "f16"), (1, 61, 1088, 1, "bf16"), (1, 45, 1056, 3, "f16")],
                          ids=lambda c: "L{}n{}k{}b{}{}".format(*c))
-def test_unaligned_rows_gemv_forced_plan(case, plan, monkeypatch):
+def test_unaligned_rows_gemv_forced_plan(case, plan, force):
     """Every lane mapping on rows at all byte offsets (an odd block count ignores a
     forced P = 2 and takes single-block units)."""
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")
-    monkeypatch.setenv("RFP4_GEMV_PLAN", plan)
+    force(gemv_kernel="dot", gemv_plan=tuple(map(int, plan.split(":"))))
     layout, n, k, batch, dt = case
     rng = np.random.default_rng(8200 + n + k)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
@@ -822,10 +814,10 @@ def test_unaligned_rows_gemm(case):
 @pytest.mark.parametrize("plan", ["main", "tail", "tail2", "tail4", "msplit3"])
 @pytest.mark.parametrize("case", [(0, 100, 200, 96), (1, 130, 264, 544), (0, 257, 300, 1376)],
                          ids=lambda c: "L{}m{}n{}k{}".format(*c))
-def test_unaligned_rows_gemm_forced_tile_size(case, plan, monkeypatch):
+def test_unaligned_rows_gemm_forced_tile_size(case, plan, force):
     """The zero-filled k tail in each tile configuration and in every split part
     (k = 544: 17 blocks, so four splits of the five step pairs)."""
-    monkeypatch.setenv("RFP4_GEMM_PLAN", plan)
+    force(gemm_plan=plan)
     layout, m, n, k = case
     rng = np.random.default_rng(8500 + m + n + k)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
@@ -846,7 +838,7 @@ def test_unaligned_rows_gemm_tail_ignores_values_past_k():
     ad = torch.full((m, lda), float("nan"), dtype=torch.bfloat16, device=DEV)
     ad[:, :k] = a.to(DEV)
     c = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
-    st = R.lib().rfp4_gemm(R._ptr(dev(w)), layout, n, k, R._ptr(ad), m, lda, R._ptr(c), n, R._stream(None))
+    st = R.lib().rfp4_gemm(R._ptr(dev(w)), layout, n, k, R._ptr(ad), m, lda, R._ptr(c), n, R._stream(None))  # noqa
     assert st == R.RFP4_OK
     torch.cuda.synchronize()
     c_ref, den = O.gemm(w, layout, n, k, x64(a))
@@ -891,8 +883,8 @@ MFMA_CASES = [  # layout, n, k, batch, dtype
 
 
 @pytest.mark.parametrize("case", MFMA_CASES, ids=lambda c: "L{}n{}k{}b{}{}".format(*c))
-def test_gemv_mfma(case, monkeypatch):
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+def test_gemv_mfma(case, force):
+    force(gemv_kernel="tiles")
     layout, n, k, batch, dt = case
     rng = np.random.default_rng(9000 + n + k + batch)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
@@ -901,15 +893,15 @@ def test_gemv_mfma(case, monkeypatch):
 
 
 @pytest.mark.parametrize("batch", [2, 8])
-def test_gemv_dot_product_kernel_large_batch(batch, monkeypatch):
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "0")
+def test_gemv_dot_product_kernel_large_batch(batch, force):
+    force(gemv_kernel="dot")
     w, x, cfg = synth.gemv_inputs("down", batch=batch)
     check_gemv(w, cfg["layout"], cfg["n"], cfg["k"], x)
 
 
-def test_gemv_mfma_padded_activations(monkeypatch):
+def test_gemv_mfma_padded_activations(force):
     """ldx > k and ldy > n on the matrix-core path."""
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    force(gemv_kernel="tiles")
     layout, n, k, batch = 0, 77, 768, 5
     rng = np.random.default_rng(9100)
     w = synth.weights(rng, layout, n, k)
@@ -918,8 +910,8 @@ def test_gemv_mfma_padded_activations(monkeypatch):
 
 
 @pytest.mark.parametrize("case", MULTI, ids=lambda c: "L{}p{}k{}b{}{}".format(c[0], len(c[1]), *c[2:]))
-def test_gemv_mfma_multi(case, monkeypatch):
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+def test_gemv_mfma_multi(case, force):
+    force(gemv_kernel="tiles")
     layout, ns, k, batch, dt = case
     rng = np.random.default_rng(9200 + sum(ns) + k + batch)
     ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
@@ -939,22 +931,20 @@ SPLIT_CASES = [  # layout, n, k, batch, dtype, forced split (reduced to one chun
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "L{}n{}k{}b{}{}-s{}".format(*c))
-def test_gemv_mfma_split(case, monkeypatch):
+def test_gemv_mfma_split(case, force):
     """Each tile's chunks shared by 1, 2 or 4 workgroups whose partial sums meet in the
     stream's workspace; padded output rows stay untouched."""
     layout, n, k, batch, dt, split = case
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
-    monkeypatch.setenv("RFP4_GEMV_SPLIT", str(split))
+    force(gemv_kernel="tiles", gemv_splits=int(split))
     rng = np.random.default_rng(9400 + n + k + batch)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
     x = synth.activations(rng, batch, k, dt)
     check_gemv(w, layout, n, k, x, ldy=n + 5)
 
 
-def test_gemv_mfma_split_launch_sequence(monkeypatch):
+def test_gemv_mfma_split_launch_sequence(force):
     """Launches with different splits and tile counts back to back on one stream (the
     arrival counters must be back at zero after each), then the first one again."""
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
     rng = np.random.default_rng(9450)
     shapes = [(0, 700, 2048, 4, 4), (1, 130, 6144, 8, 2), (0, 700, 2048, 4, 2), (0, 64, 5120, 2, 4),
               (0, 700, 2048, 4, 4)]
@@ -967,19 +957,18 @@ def test_gemv_mfma_split_launch_sequence(monkeypatch):
             data[(layout, n, k, batch)] = (dev(w), x.to(DEV).contiguous(), y_ref, den)
     ys = []
     for layout, n, k, batch, split in shapes:
-        monkeypatch.setenv("RFP4_GEMV_SPLIT", str(split))
         wd, xd, _, _ = data[(layout, n, k, batch)]
-        ys.append(R.rfp4_gemv(wd, layout, n, k, xd))
+        ys.append(R.rfp4_gemv(wd, layout, n, k, xd, force=R.make_force("tiles", gemv_splits=split)))
     torch.cuda.synchronize()
     for (layout, n, k, batch, _), y in zip(shapes, ys):
         _, _, y_ref, den = data[(layout, n, k, batch)]
         assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
 
 
-def test_gemv_mfma_multi_two_tiles(monkeypatch):
+def test_gemv_mfma_multi_two_tiles(force):
     """Two matrices fused at batch 7 with enough tiles for two tiles per workgroup: the
     32-row tiles of each part start at the part's first row."""
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+    force(gemv_kernel="tiles")
     layout, ns, k, batch = 0, [9000, 8008], 256, 7
     rng = np.random.default_rng(9470)
     ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
@@ -991,9 +980,8 @@ def test_gemv_mfma_multi_two_tiles(monkeypatch):
         assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
 
 
-def test_gemv_mfma_multi_split(monkeypatch):
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
-    monkeypatch.setenv("RFP4_GEMV_SPLIT", "4")
+def test_gemv_mfma_multi_split(force):
+    force(gemv_kernel="tiles", gemv_splits=4)
     layout, ns, k, batch = 1, [300, 45, 1000, 7], 6144, 5
     rng = np.random.default_rng(9460)
     ws = [synth.weights(rng, layout, n, k, stress_frac=0.01) for n in ns]
@@ -1005,8 +993,8 @@ def test_gemv_mfma_multi_split(monkeypatch):
         assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
 
 
-def test_gemv_mfma_zero_scales_give_zero(monkeypatch):
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
+def test_gemv_mfma_zero_scales_give_zero(force):
+    force(gemv_kernel="tiles")
     layout, n, k, batch = 0, 40, 512, 4
     w = synth.weights(np.random.default_rng(9300), layout, n, k).reshape(n, k // 32, 18)
     w[:, :, 16:] = 0
@@ -1017,14 +1005,14 @@ def test_gemv_mfma_zero_scales_give_zero(monkeypatch):
 
 # ------------------------------------------------------------------ graph capture
 
-def test_graph_replay_matches_eager(monkeypatch):
+def test_graph_replay_matches_eager(force):
     """Every entry point captured into one HIP graph (batch-1 and batch-4 GEMV, a
     batch-4 GEMV on long rows whose tiles split, fused two-matrix GEMVs at batch 1 and
     4, a GEMM with split k, dequant, encoder)
     and replayed three times, with eager work between the replays, gives exactly the
     eager results. Everything runs on the capture stream first so that the workspaces
     exist before the capture, as the header asks."""
-    monkeypatch.setenv("RFP4_GEMM_PLAN", "tail2")
+    force(gemm_plan="tail2")
     rng = np.random.default_rng(9500)
     layout, n, k = 0, 1040, 2048
     wd = dev(synth.weights(rng, layout, n, k))
@@ -1081,11 +1069,10 @@ def test_graph_replay_matches_eager(monkeypatch):
             assert torch.equal(v, eager[key]), (key, rep)
 
 
-def test_gemv_split_two_streams(monkeypatch):
+def test_gemv_split_two_streams(force):
     """Split-tile GEMVs interleaved on two streams: each stream has its own workspace
     (partial sums and arrival counters), so concurrent launches do not mix."""
-    monkeypatch.setenv("RFP4_GEMV_MFMA", "1")
-    monkeypatch.setenv("RFP4_GEMV_SPLIT", "2")
+    force(gemv_kernel="tiles", gemv_splits=2)
     rng = np.random.default_rng(9600)
     layout, n, k = 1, 640, 12288
     ws = [synth.weights(rng, layout, n, k) for _ in range(2)]
@@ -1108,13 +1095,13 @@ def test_gemv_split_two_streams(monkeypatch):
 
 
 @pytest.mark.parametrize("mode,batch", [("0", 1), ("", 1), ("1", 4), ("1", 8)])
-def test_gemv_vocab_rows_sampled(mode, batch, monkeypatch):
+def test_gemv_vocab_rows_sampled(mode, batch, force):
     """A vocabulary-sized matrix (152064 x 5120 dual, 438 MB packed: the decode LM head)
     on each kernel (batch 1: the dot-product kernel forced, and the default, the tall
     matrix-core kernel), checked on a seeded sample of rows that includes the first and
     the last."""
     if mode:
-        monkeypatch.setenv("RFP4_GEMV_MFMA", mode)
+        force(gemv_kernel={"0": "dot", "1": "tiles"}[mode])
     layout, n, k = 0, 152064, 5120
     rng = np.random.default_rng(9700 + batch)
     w = synth.weights(rng, layout, n, k)
@@ -1123,3 +1110,54 @@ def test_gemv_vocab_rows_sampled(mode, batch, monkeypatch):
     rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], rng.choice(n, 96, replace=False)]))
     y_ref, den = O.gemv_rows(w, layout, n, k, x64(x), rows)
     assert O.normalized_error(y[:, rows], y_ref, den) <= TOL
+
+
+def test_workspace_growth_keeps_captured_graphs_valid():
+    """A graph captured with a split GEMM and a split-tile GEMV, then eager calls on the
+    same stream with larger shapes (the GEMM's partial sums outgrow the stream's
+    workspace, so the library moves to a larger buffer and keeps the old one), then
+    replays with more eager work between them: every replay gives the eager results of
+    the captured shapes bit for bit, and the larger calls stay correct."""
+    rng = np.random.default_rng(9800)
+    fg = R.make_force(gemm_plan="tail2")
+    fv = R.make_force("tiles", gemv_splits=2)
+    layout, n, k = 0, 1040, 2048
+    wd = dev(synth.weights(rng, layout, n, k))
+    a = synth.activations(rng, 200, k, "bf16").to(DEV).contiguous()
+    vl, vn, vk = 1, 520, 12288
+    wv = dev(synth.weights(rng, vl, vn, vk))
+    xv = synth.activations(rng, 4, vk, "bf16").to(DEV).contiguous()
+    big_w = synth.weights(rng, layout, 4096, k)
+    big_a = synth.activations(rng, 1024, k, "bf16")
+    big_wd, big_ad = dev(big_w), big_a.to(DEV).contiguous()
+    big_vw = synth.weights(rng, vl, 1000, vk)
+    big_vx = synth.activations(rng, 8, vk, "bf16")
+    big_vwd, big_vxd = dev(big_vw), big_vx.to(DEV).contiguous()
+    c = torch.empty((200, n), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((4, vn), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        R.rfp4_gemm(wd, layout, n, k, a, c, force=fg)  # creates the stream's workspaces
+        R.rfp4_gemv(wv, vl, vn, vk, xv, y, force=fv)
+        s.synchronize()
+        eager_c, eager_y = c.clone(), y.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            R.rfp4_gemm(wd, layout, n, k, a, c, force=fg)
+            R.rfp4_gemv(wv, vl, vn, vk, xv, y, force=fv)
+        big_c = R.rfp4_gemm(big_wd, layout, 4096, k, big_ad, force=fg)  # outgrows the workspace
+        big_y = R.rfp4_gemv(big_vwd, vl, 1000, vk, big_vxd, force=fv)
+        s.synchronize()
+        for rep in range(3):
+            c.zero_()
+            y.zero_()
+            g.replay()
+            R.rfp4_gemm(big_wd, layout, 4096, k, big_ad, big_c, force=fg)
+            s.synchronize()
+            assert torch.equal(c, eager_c), rep
+            assert torch.equal(y, eager_y), rep
+    c_ref, den = O.gemm(big_w, layout, 4096, k, x64(big_a))
+    assert gemm_error(big_c.to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
+    y_ref, vden = O.gemv(big_vw, vl, 1000, vk, x64(big_vx))
+    assert O.normalized_error(big_y.cpu().numpy(), y_ref, vden) <= TOL

@@ -15,6 +15,7 @@ import torch
 import gemm_rfp4_block_amd as R
 import oracle.rfp4_oracle as O
 import synth
+from tests.abi_calls import gemm_raw, gemv_raw
 from tests.test_gpu_parity import gemm_error
 
 pytestmark = pytest.mark.gpu
@@ -39,16 +40,15 @@ def round8(v):
 
 
 @pytest.mark.parametrize("case", range(40), ids=lambda i: f"gemv{i}")
-def test_random_gemv(case, monkeypatch):
+def test_random_gemv(case):
     rng = np.random.default_rng(71000 + case)
     layout = int(rng.integers(0, 2))
     n = log_uniform(rng, 1, 400)
     k = 32 * log_uniform(rng, 1, 300)
     batch = int(rng.integers(1, 9))
     dt = ("f16", "bf16")[int(rng.integers(0, 2))]
-    mode = (None, "0", "1")[int(rng.integers(0, 3))]
-    if mode is not None:
-        monkeypatch.setenv("RFP4_GEMV_MFMA", mode)
+    mode = (None, "dot", "tiles")[int(rng.integers(0, 3))]
+    f = R.make_force(mode) if mode is not None else None
     ldx = k + (0, 8, 24)[int(rng.integers(0, 3))]
     ldy = n + (0, 3)[int(rng.integers(0, 2))]
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
@@ -56,8 +56,7 @@ def test_random_gemv(case, monkeypatch):
     xd = torch.zeros((batch, ldx), dtype=x.dtype, device=DEV)
     xd[:, :k] = x.to(DEV)
     y = torch.full((batch, ldy), float("nan"), dtype=torch.float32, device=DEV)
-    st = R.lib().rfp4_gemv(R._ptr(dev(w)), layout, n, k, R._ptr(xd), R._xdtype(xd), batch, ldx,
-                           R._ptr(y), ldy, R._stream(None))
+    st = gemv_raw(dev(w), layout, n, k, xd, batch, ldx, y, ldy, force=f)
     assert st == R.RFP4_OK, R.rfp4_status_string(st)
     torch.cuda.synchronize()
     out = y.cpu().numpy()
@@ -70,22 +69,20 @@ GEMM_PLANS = (None, "main", "tail", "tail2", "tail4", "msplit2", "msplit3", "nos
 
 
 @pytest.mark.parametrize("case", range(24), ids=lambda i: f"gemm{i}")
-def test_random_gemm(case, monkeypatch):
+def test_random_gemm(case):
     rng = np.random.default_rng(72000 + case)
     layout = int(rng.integers(0, 2))
     m = log_uniform(rng, 1, 300)
     n = log_uniform(rng, 1, 400)
     k = 32 * log_uniform(rng, 1, 100)
     plan = GEMM_PLANS[int(rng.integers(0, len(GEMM_PLANS)))]
-    if plan is not None:
-        monkeypatch.setenv("RFP4_GEMM_PLAN", plan)
+    f = R.make_force(gemm_plan=plan) if plan is not None else None
     ldc = round8(n) + 8
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
     a = synth.activations(rng, m, k, "bf16")
     c = torch.full((m, ldc), float("nan"), dtype=torch.bfloat16, device=DEV)
     ad = a.to(DEV).contiguous()
-    st = R.lib().rfp4_gemm(R._ptr(dev(w)), layout, n, k, R._ptr(ad), m, k, R._ptr(c), ldc,
-                           R._stream(None))
+    st = gemm_raw(dev(w), layout, n, k, ad, m, k, c, ldc, force=f)
     assert st == R.RFP4_OK, R.rfp4_status_string(st)
     torch.cuda.synchronize()
     out = c.to(torch.float64).cpu().numpy()
