@@ -25,10 +25,13 @@ RFP4_ERR_SHAPE = 2
 RFP4_ERR_UNSUPPORTED = 3
 RFP4_ERR_NONFINITE_SCALE = 4
 RFP4_ERR_HIP = 5
+RFP4_ERR_SCRATCH = 6
+GEMM_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = ("rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
             "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
-            "rfp4_gemm_dequant", "rfp4_quantize", "rfp4_gemv_multi_ex", "rfp4_gemm_ex")
+            "rfp4_gemm_dequant", "rfp4_quantize", "rfp4_gemv_multi_ex", "rfp4_gemm_ex",
+            "rfp4_gemm_noalloc")
 MAX_GEMV_PARTS = 8
 
 # rfp4_gemv_kernel and rfp4_gemm_plan (include/rfp4.h)
@@ -102,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.rfp4_gemv_multi_ex.restype = c_int
     L.rfp4_gemm_ex.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, fp, c_vp]
     L.rfp4_gemm_ex.restype = c_int
+    L.rfp4_gemm_noalloc.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, fp, c_vp]
+    L.rfp4_gemm_noalloc.restype = c_int
     L.rfp4_dequant_bf16.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_vp]
     L.rfp4_dequant_bf16.restype = c_int
     L.rfp4_gemm_dequant.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]
@@ -253,6 +258,16 @@ def rfp4_gemm(w, layout: int, n: int, k: int, a, c=None, stream=None, force: For
     return c
 
 
+def rfp4_gemm_noalloc(w, layout: int, n: int, k: int, a, c, stream=None, force: Force | None = None):
+    """C = A W^T like rfp4_gemm, with split plans' partial sums in the library's static
+    per-GPU scratch array (no allocation); ``c`` (m, n) bf16 must be given."""
+    m = a.shape[0]
+    _check(lib().rfp4_gemm_noalloc(_ptr(w), layout, n, k, _ptr(a), m, a.stride(0), _ptr(c), c.stride(0),
+                                   ctypes.byref(force) if force is not None else None, _stream(stream)),
+           "rfp4_gemm_noalloc")
+    return c
+
+
 def rfp4_gemm_dequant(w, layout: int, n: int, k: int, a, wbuf=None, c=None, stream=None):
     """C = A W^T computed as bf16 dequantization into ``wbuf`` (n, k) plus a dense bf16
     GEMM (rocBLAS)."""
@@ -291,5 +306,5 @@ __all__ = [
     "rfp4_block_bytes", "rfp4_row_bytes", "rfp4_status_string", "rfp4_validate",
     "rfp4_dequant", "rfp4_dequant_bf16", "rfp4_gemv", "rfp4_gemv_multi", "rfp4_gemm",
     "rfp4_gemm_dequant", "rfp4_quantize", "RFP4_F32", "MAX_GEMV_PARTS", "Force", "make_force",
-    "GEMV_KERNEL", "GEMM_PLAN",
+    "GEMV_KERNEL", "GEMM_PLAN", "rfp4_gemm_noalloc", "RFP4_ERR_SCRATCH", "GEMM_SCRATCH_BYTES",
 ]

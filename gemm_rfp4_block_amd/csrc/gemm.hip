@@ -969,4 +969,74 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
   return run_gemm(w, layout, n, k, a, m, lda, c, ldc, force.gemm_plan, 512.0 * 1024 * 1024, get_ws, stream);
 }
 
+// ---------------------------------------------------------------- allocation-free GEMM
+//
+// The partial sums of split plans live in `scratch`, a static device array (one copy
+// per GPU the library runs on, kept until the process ends) instead of a workspace, so
+// rfp4_gemm_noalloc calls no allocator. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): its device address is
+// looked up once per device with that device current and kept.
+static __device__ __align__(256) float scratch[kGemmScratchBytes / sizeof(float)];
+
+namespace {
+
+// Device address of `scratch` on the current device (looked up on the first call per
+// device, under a lock; threads that come later read the kept address).
+hipError_t scratch_address(float** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = static_cast<float*>(addr[dev]);
+  return hipSuccess;
+}
+
+}  // namespace
+
+// Partial-sum bytes of the plan rfp4_gemm_noalloc would run for this shape (0 = no
+// split); the same planner as launch_gemm_noalloc, so a caller can reject a shape
+// before any launch.
+double gemm_noalloc_plan_bytes(int64_t n, int64_t k, int64_t m, const Force& force) {
+  const int nb = static_cast<int>(k / 32);
+  const int cus = device_cu_count();
+  const int64_t max_m = int64_t(1) << 20;
+  double need = 0.0;
+  for (int64_t m_off = 0; m_off < m; m_off += max_m) {
+    const int mc = static_cast<int>(m - m_off < max_m ? m - m_off : max_m);
+    const Plan plan = choose_plan(mc, n, nb, cus, force.gemm_plan, static_cast<double>(kGemmScratchBytes));
+    const double b = (plan.main_splits > 1 ? static_cast<double>(plan.main_tiles) * plan.main_splits *
+                                                 MainCfg::BM * MainCfg::BN * 4.0
+                                           : 0.0) +
+                     (plan.splits > 1 ? static_cast<double>(plan.tail_tiles) * plan.splits *
+                                            TailCfg::BM * TailCfg::BN * 4.0
+                                      : 0.0);
+    need = std::max(need, b);
+  }
+  return need;
+}
+
+hipError_t launch_gemm_noalloc(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
+                               int64_t m, int64_t lda, uint16_t* c, int64_t ldc, const Force& force,
+                               hipStream_t stream) {
+  float* base = nullptr;
+  const hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return e;
+  auto get_ws = [&](size_t bytes, float** out) {
+    if (bytes > kGemmScratchBytes) return false;  // never: the planner keeps within it
+    *out = base;
+    return true;
+  };
+  return run_gemm(w, layout, n, k, a, m, lda, c, ldc, force.gemm_plan, static_cast<double>(kGemmScratchBytes),
+                  get_ws, stream);
+}
+
 }  // namespace rfp4

@@ -78,6 +78,9 @@ const char* rfp4_status_string(int status) {
     case RFP4_ERR_UNSUPPORTED: return "unsupported layout, dtype or alignment";
     case RFP4_ERR_NONFINITE_SCALE: return "non-finite scale byte (low seven bits all ones)";
     case RFP4_ERR_HIP: return "HIP runtime error at launch";
+    case RFP4_ERR_SCRATCH:
+      return "the forced GEMM plan needs more partial-sum memory than the allocation-free entry point's "
+             "static scratch array holds";
     default: return "unknown status";
   }
 }
@@ -208,6 +211,21 @@ rfp4_status rfp4_gemm_ex(const void* w, int layout, int64_t n, int64_t k, const 
                                     static_cast<const uint16_t*>(a), m, lda,
                                     static_cast<uint16_t*>(c), ldc, f,
                                     static_cast<hipStream_t>(stream)));
+}
+
+rfp4_status rfp4_gemm_noalloc(const void* w, int layout, int64_t n, int64_t k, const void* a,
+                              int64_t m, int64_t lda, void* c, int64_t ldc, const rfp4_force* force,
+                              void* stream) {
+  rfp4::Force f;
+  if (check_force(force, &f) != RFP4_OK) return RFP4_ERR_UNSUPPORTED;
+  rfp4_status st = check_gemm(w, layout, n, k, a, m, lda, c, ldc);
+  if (st != RFP4_OK) return st;
+  if (rfp4::gemm_noalloc_plan_bytes(n, k, m, f) > static_cast<double>(RFP4_GEMM_SCRATCH_BYTES))
+    return RFP4_ERR_SCRATCH;
+  return from_hip(rfp4::launch_gemm_noalloc(static_cast<const uint8_t*>(w), layout, n, k,
+                                            static_cast<const uint16_t*>(a), m, lda,
+                                            static_cast<uint16_t*>(c), ldc, f,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 rfp4_status rfp4_gemm(const void* w, int layout, int64_t n, int64_t k, const void* a,

@@ -76,4 +76,14 @@ hipError_t launch_gemm(const uint8_t* w, int layout, int64_t n, int64_t k, const
                        int64_t m, int64_t lda, uint16_t* c, int64_t ldc, const Force& force,
                        hipStream_t stream);
 
+// The allocation-free GEMM: partial sums of split plans in a static device array of
+// kGemmScratchBytes per GPU; plans are chosen among those that fit it, and a forced
+// plan that needs more is rejected by the API layer (gemm_noalloc_plan_bytes).
+constexpr size_t kGemmScratchBytes = RFP4_GEMM_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+double gemm_noalloc_plan_bytes(int64_t n, int64_t k, int64_t m, const Force& force);
+hipError_t launch_gemm_noalloc(const uint8_t* w, int layout, int64_t n, int64_t k, const uint16_t* a,
+                               int64_t m, int64_t lda, uint16_t* c, int64_t ldc, const Force& force,
+                               hipStream_t stream);
+
 }  // namespace rfp4

@@ -67,7 +67,9 @@ typedef enum rfp4_status {
                                     outside 1..8, or a leading dimension too small */
   RFP4_ERR_UNSUPPORTED = 3,      /* unknown layout or dtype, or an alignment rule broken */
   RFP4_ERR_NONFINITE_SCALE = 4,  /* rfp4_validate found a non-finite scale byte */
-  RFP4_ERR_HIP = 5               /* the HIP runtime reported an error at launch */
+  RFP4_ERR_HIP = 5,              /* the HIP runtime reported an error at launch */
+  RFP4_ERR_SCRATCH = 6           /* rfp4_gemm_noalloc: the forced plan's partial sums need
+                                    more than RFP4_GEMM_SCRATCH_BYTES */
 } rfp4_status;
 
 typedef enum rfp4_layout {
@@ -234,6 +236,25 @@ RFP4_API rfp4_status rfp4_gemv_multi_ex(int count, const void* const* w, const i
 RFP4_API rfp4_status rfp4_gemm_ex(const void* w, int layout, int64_t n, int64_t k, const void* a,
                                   int64_t m, int64_t lda, void* c, int64_t ldc,
                                   const rfp4_force* force, void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. rfp4_gemm_ex with the same arguments,
+ * checks and result, except where its split plans keep their fp32 partial sums: in a
+ * static device array of RFP4_GEMM_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends, not in a workspace. No call allocates, frees or
+ * synchronizes anything. The cost model chooses among the plans whose partial sums fit
+ * the array (where rfp4_gemm's plan fits, that is the same plan, and the outputs are
+ * bit-identical); a forced plan (force->gemm_plan) that needs more is rejected with
+ * RFP4_ERR_SCRATCH before any launch. Every call on one GPU shares that GPU's array and
+ * leaves its contents behind (the partial sums are written before they are read, so
+ * nothing needs clearing): calls that overlap in time on one GPU (other streams, other
+ * threads, graph replays running concurrently) race on it and must be ordered by the
+ * caller. The first call on a device looks up the array's device address (no
+ * allocation). */
+#define RFP4_GEMM_SCRATCH_BYTES (32u << 20)
+RFP4_API rfp4_status rfp4_gemm_noalloc(const void* w, int layout, int64_t n, int64_t k,
+                                       const void* a, int64_t m, int64_t lda, void* c,
+                                       int64_t ldc, const rfp4_force* force, void* stream);
 
 /* Dequantize-then-multiply prefill, the comparison baseline of rfp4_gemm ("Kernel
  * System" lists dequantize + dense GEMM beside the fused w4a16_gemm): W is expanded

@@ -63,7 +63,7 @@ def test_block_and_row_bytes(L):
 
 
 def test_status_strings(L):
-    for st in range(6):
+    for st in range(7):
         assert R.rfp4_status_string(st)
     assert R.rfp4_status_string(99) == "unknown status"
 
