@@ -15,10 +15,14 @@ encoding, and the 64-layer decode sweep (448 GEMVs, 12.3 GB).
 The GEMV extras (batched, down-projection, fused) are timed as HIP graphs of 100
 launches replayed back to back (event time of a replay / 100), so that the GPU never
 waits for the host between these short kernels; the longer kernels (GEMM, dequant,
-encoder) by HIP events around every launch on the stream they run on. The CPU baseline
-times the fp64 oracle on the host.
+encoder) by HIP events around every launch on the stream they run on. A plain
+streaming read of the same weight copies (librfp4_bench.so) gives the HBM read rate a
+kernel of this size reaches. The CPU baseline times the fp64 oracle on the host on every
+workload (tiny, up-projection, down-projection at each batch, the full prefill GEMM).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-sweep]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-sweep] [--no-gemm]
+       [--guard REFERENCE_JSON]   (exit 3 on a slowdown of more than 10 % against a saved line)
+       [--pmc-mode | --pmc-gemm | --pmc-down | --sweep-only]   (short runs for rocprofv3)
 """
 
 from __future__ import annotations
@@ -181,6 +185,229 @@ def bench_gemv_graph(torch, R, copies, layout, n, k, x, y, steps, warmup):
     return (t1 - t0) * 1e3, ev0.elapsed_time(ev1), replay_ok
 
 
+READ_UNROLL, READ_WGS_PER_CU = 1, 8  # the fastest launch shape of a sweep on MI355X
+
+
+def read_ceiling(torch, copies, w_bytes, dev):
+    """Plain streaming read (librfp4_bench.so) of the rotated weight copies (the bytes the
+    headline GEMV reads, one 50 MB copy per launch) and of one 800 MiB buffer: the HBM
+    read rate a kernel of that size reaches, for comparison with the GEMV."""
+    import ctypes
+
+    lib_path = os.path.join(ROOT, "gemm_rfp4_block_amd", "_lib", "librfp4_bench.so")
+    B = ctypes.CDLL(lib_path)
+    B.rfp4bench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def read(t, nbytes):
+        st = B.rfp4bench_read(ctypes.c_void_p(t.data_ptr()), nbytes, READ_UNROLL, READ_WGS_PER_CU,
+                              ctypes.c_void_p(sink.data_ptr()),
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"rfp4bench_read failed: {st}")
+
+    nc = len(copies)
+    fn = lambda i: read(copies[i % nc], w_bytes)
+    warm_up(torch, fn, 0.1)
+    us = graph_us(torch, fn, 100)
+    big = torch.empty(800 * 2**20, dtype=torch.uint8, device=dev).fill_(3)
+    fnb = lambda i: read(big, big.numel())
+    warm_up(torch, fnb, 0.1)
+    usb = graph_us(torch, fnb, 20)
+    del big
+    return {"rotated_50MB": {"us": round(us, 3), "GB/s": round(w_bytes / (us * 1e-6) / 1e9, 1),
+                             "bytes": w_bytes, "copies": nc},
+            "single_800MiB": {"us": round(usb, 2), "GB/s": round(800 * 2**20 / (usb * 1e-6) / 1e9, 1)},
+            "kernel": f"rfp4bench_read (16-byte loads, {READ_UNROLL} per lane in flight, "
+                      f"{READ_WGS_PER_CU} 256-thread workgroups per CU)"}
+
+
+GUARD_KEYS = [  # (path in the JSON line, True if lower is better)
+    (("roofline", "avg_launch_us"), True),
+    (("gemm", "mean_us"), True),
+    (("extra", "gemv_down_fast_bf16", "b1", "mean_us"), True),
+    (("extra", "gemv_down_fast_bf16", "b2", "mean_us"), True),
+    (("extra", "gemv_down_fast_bf16", "b4", "mean_us"), True),
+    (("extra", "gemv_down_fast_bf16", "b8", "mean_us"), True),
+    (("extra", "gemv_up_dual_f16_batched", "b8", "mean_us"), True),
+    (("extra", "gemv_multi", "gate_up", "fused_mean_us"), True),
+    (("extra", "gemv_multi", "qkv", "fused_mean_us"), True),
+    (("extra", "sweep_64_layers_fused", "ms_per_sweep"), True),
+    (("extra", "dequant_up", "mean_us"), True),
+]
+
+
+def guard(result, ref_path, tol=0.10):
+    """Regression guard: every GUARD_KEYS entry of `result` against the same entry of a
+    committed reference line; a time more than `tol` above the reference is a
+    regression. Returns (ok, report)."""
+    with open(ref_path) as f:
+        ref = json.loads(f.read().strip().splitlines()[-1])
+
+    def get(d, path):
+        for p in path:
+            if not isinstance(d, dict) or p not in d:
+                return None
+            d = d[p]
+        return d
+
+    report, ok = {}, True
+    for path, lower_better in GUARD_KEYS:
+        a, b = get(result, path), get(ref, path)
+        if a is None or b is None:
+            continue
+        ratio = a / b if lower_better else b / a
+        bad = ratio > 1.0 + tol
+        ok = ok and not bad
+        report[".".join(path)] = {"now": a, "reference": b, "slowdown": round(ratio, 4), "regression": bad}
+    return ok, report
+
+
+def cpu_baseline(synth, w_host, x_host, layout, n, k, alg_bytes):
+    """The fp64 oracle (dequantization, fp64 contraction and the |w||x| denominator) timed
+    on the host: the tiny GEMV, the up-projection GEMV (the headline unit, GB/s), the
+    down-projection GEMV at batch 1/2/4/8 and the full prefill GEMM once, each with its
+    own wall time. `cores` is the number of BLAS threads the oracle's matrix products
+    ran on; `host_cores` the CPUs this process may use."""
+    import oracle.rfp4_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+
+    def timed(fn, min_s, max_reps):
+        reps, t = 0, 0.0
+        while (t < min_s or reps == 0) and reps < max_reps:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            reps += 1
+        return reps, t
+
+    per = {}
+    tw, tx, tcfg = synth.gemv_inputs("tiny")
+    txh = tx.double().numpy()
+    reps, t = timed(lambda: O.gemv(tw, tcfg["layout"], tcfg["n"], tcfg["k"], txh), 0.5, 2000)
+    tb = tw.size + tcfg["k"] * 2 + tcfg["n"] * 4
+    per["tiny_gemv"] = {"value": round(tb * reps / t / 1e9, 4), "unit": "GB/s", "reps": reps, "s": round(t, 2)}
+    xh = x_host.double().numpy()
+    reps, t = timed(lambda: O.gemv(w_host, layout, n, k, xh), 4.0, 16)
+    up = {"value": round(alg_bytes * reps / t / 1e9, 4), "unit": "GB/s", "reps": reps, "s": round(t, 2)}
+    per["up_gemv"] = up
+    dw, dx, dcfg = synth.gemv_inputs("down")
+    for b in (1, 2, 4, 8):
+        xb = dx[:b].double().numpy()
+        reps, t = timed(lambda: O.gemv(dw, dcfg["layout"], dcfg["n"], dcfg["k"], xb), 0.0, 1)
+        bts = dw.size + b * dcfg["k"] * 2 + b * dcfg["n"] * 4
+        per[f"down_gemv_b{b}"] = {"value": round(bts * reps / t / 1e9, 4), "unit": "GB/s", "reps": reps,
+                                  "s": round(t, 2)}
+    gw, ga, gcfg = synth.gemm_inputs("prefill")
+    gah = ga.double().numpy()
+    reps, t = timed(lambda: O.gemm(gw, gcfg["layout"], gcfg["n"], gcfg["k"], gah), 0.0, 1)
+    flops = 2.0 * gcfg["m"] * gcfg["n"] * gcfg["k"]
+    per["prefill_gemm"] = {"value": round(flops * reps / t / 1e12, 4), "unit": "TFLOP/s", "reps": reps,
+                           "s": round(t, 2)}
+    total_s = sum(v["s"] for v in per.values())
+    return {"value": up["value"], "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "host_cores": len(os.sched_getaffinity(0)),
+            "sample": f"up-projection GEMV (17408 x 5120 dual, fp16 x, batch 1) x {up['reps']} in {up['s']} s; "
+                      f"per_workload: the tiny GEMV repeated, the down-projection GEMV once per batch, "
+                      f"the full 2048 x 17408 x 5120 prefill GEMM once; {total_s:.1f} s of oracle work in all",
+            "per_workload": per}
+
+
+def run_sweeps(torch, R, synth, dev, reps=5):
+    """The 64-layer decode sweep (448 dual GEMVs, 12.3 GB of weights, a fresh fp16 x per
+    GEMV) as one captured graph, and the same layers with fused launches (q+k+v and
+    gate+up share their x); wall time per sweep over `reps` replays after an untimed
+    settling replay."""
+    out = {}
+    mats, xs, ys, total = [], [], [], 0
+    for layer in range(synth.SWEEP_LAYERS):
+        for pi, (name, sn, sk) in enumerate(synth.SWEEP_SHAPES):
+            seed = 10_000 + layer * 16 + pi
+            mats.append((synth.weights_device(0, sn, sk, seed, dev), sn, sk))
+            xs.append(synth.activations_device(1, sk, "f16", seed, dev))
+            ys.append(torch.empty((1, sn), dtype=torch.float32, device=dev))
+            total += sn * synth.row_bytes(0, sk) + sk * 2 + sn * 4
+    torch.cuda.synchronize()
+
+    def sweep():
+        for (wm, sn, sk), xx, yy in zip(mats, xs, ys):
+            R.rfp4_gemv(wm, 0, sn, sk, xx, yy)
+
+    sweep()
+    g = torch.cuda.CUDAGraph()
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s2):
+        sweep()
+    torch.cuda.current_stream().wait_stream(s2)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s2):
+        sweep()
+    g.replay()
+    torch.cuda.synchronize()
+    settle_graph(torch, g, 0.3)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    sweep_ms = (time.perf_counter() - t0) * 1e3 / reps
+    out["sweep_64_layers"] = {"GB/s": round(total / (sweep_ms * 1e-3) / 1e9, 1), "bytes": total,
+                                "ms_per_sweep": round(sweep_ms, 3), "launches": len(mats),
+                                "tokens_per_s_equivalent": round(1e3 / sweep_ms, 1)}
+    log(f"sweep: {sweep_ms:.3f} ms -> {out['sweep_64_layers']['GB/s']:.0f} GB/s")
+
+    # fused: per layer one launch for q+k+v (shared x), o, gate+up (shared x), down
+    nsh = len(synth.SWEEP_SHAPES)
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    fcalls, ftotal = [], 0
+    for layer in range(synth.SWEEP_LAYERS):
+        for gidx in groups:
+            ws_ = [mats[layer * nsh + j][0] for j in gidx]
+            ns_ = [mats[layer * nsh + j][1] for j in gidx]
+            kk = mats[layer * nsh + gidx[0]][2]
+            xx = xs[layer * nsh + gidx[0]]
+            yy = [ys[layer * nsh + j] for j in gidx]
+            fcalls.append((ws_, ns_, kk, xx, yy))
+            ftotal += sum(n * synth.row_bytes(0, kk) for n in ns_) + kk * 2 + sum(ns_) * 4
+
+    def fsweep():
+        for ws_, ns_, kk, xx, yy in fcalls:
+            R.rfp4_gemv_multi(ws_, 0, ns_, kk, xx, yy)
+
+    fsweep()
+    g2 = torch.cuda.CUDAGraph()
+    s3 = torch.cuda.Stream()
+    s3.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s3):
+        fsweep()
+    torch.cuda.current_stream().wait_stream(s3)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g2, stream=s3):
+        fsweep()
+    g2.replay()
+    torch.cuda.synchronize()
+    settle_graph(torch, g2, 0.3)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g2.replay()
+    torch.cuda.synchronize()
+    fsweep_ms = (time.perf_counter() - t0) * 1e3 / reps
+    out["sweep_64_layers_fused"] = {"GB/s": round(ftotal / (fsweep_ms * 1e-3) / 1e9, 1), "bytes": ftotal,
+                                      "ms_per_sweep": round(fsweep_ms, 3), "launches": len(fcalls),
+                                      "tokens_per_s_equivalent": round(1e3 / fsweep_ms, 1)}
+    log(f"sweep fused: {fsweep_ms:.3f} ms -> {out['sweep_64_layers_fused']['GB/s']:.0f} GB/s")
+    del mats, xs, ys, fcalls, g, g2
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +421,13 @@ def main():
                          "512 MiB device copy (the byte-count calibration), then exit")
     ap.add_argument("--pmc-gemm", action="store_true",
                     help="for rocprofv3 --pmc: a few prefill GEMM launches, then exit")
+    ap.add_argument("--pmc-down", action="store_true",
+                    help="for rocprofv3 --pmc: a few down-projection GEMV launches at batch 1 and 8, then exit")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="for rocprofv3 --kernel-trace: only the two 64-layer decode sweeps (a few replays each)")
+    ap.add_argument("--guard", metavar="REFERENCE_JSON",
+                    help="compare the run with a committed reference line; exit 3 if any guarded time "
+                         "is more than 10 %% above (throughput more than 10 %% below) the reference")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the ROCmFP4 "
@@ -227,6 +461,28 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"pmc gemm mode done: 8 prefill GEMM launches, one copy of {src.numel()} bytes")
+        return
+
+    if args.pmc_down:
+        wd_host, xd_host, dcfg = synth.gemv_inputs("down")
+        dn, dk, dl = dcfg["n"], dcfg["k"], dcfg["layout"]
+        dcopies = rotation_copies(torch, R, dl, dn, dk, wd_host, dev, 200)
+        for b in (1, 8):
+            xb = xd_host[:b].contiguous().to(dev)
+            yb = torch.empty((b, dn), dtype=torch.float32, device=dev)
+            for i in range(12):
+                R.rfp4_gemv(dcopies[i % len(dcopies)], dl, dn, dk, xb, yb)
+        src = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("pmc down mode done: 12 down-projection GEMVs at batch 1 and 8, one copy of 512 MiB")
+        return
+
+    if args.sweep_only:
+        sw = run_sweeps(torch, R, synth, dev, reps=3)
+        log(json.dumps(sw))
         return
 
     # ---------------- headline: up-projection GEMV, dual, fp16, batch 1
@@ -293,6 +549,15 @@ def main():
     extra = {"gemv_up_graph_replay_matches_eager": replay_ok,
              "gemv_up_direct_launches": {"us_per_launch": round(direct_us, 3),
                                          "GB/s": round(alg_bytes / (direct_us * 1e-6) / 1e9, 1)}}
+    # ---------------- HBM read ceiling: a plain streaming read of the same rotated 50 MB
+    # weight copies, and of one 800 MiB buffer (graph-replayed like the GEMV extras)
+    extra["hbm_read_ceiling"] = read_ceiling(torch, copies, w_bytes, dev)
+    extra["hbm_read_ceiling"]["gemv_up_fraction_of_50MB_read"] = round(
+        extra["hbm_read_ceiling"]["rotated_50MB"]["us"] / launch_us, 4)
+    log(f"hbm read ceiling: 50 MB {extra['hbm_read_ceiling']['rotated_50MB']['us']:.2f} us "
+        f"({extra['hbm_read_ceiling']['rotated_50MB']['GB/s']:.0f} GB/s), 800 MiB "
+        f"{extra['hbm_read_ceiling']['single_800MiB']['GB/s']:.0f} GB/s; the GEMV runs at "
+        f"{extra['hbm_read_ceiling']['gemv_up_fraction_of_50MB_read']:.1%} of the 50 MB read rate")
     # ---------------- up-projection GEMV at batch 2/4/8 (the matrix-core kernel)
     xs_host = synth.activations(np.random.default_rng(11), 8, k, "f16")
     up_batched = {}
@@ -426,113 +691,16 @@ def main():
         torch.cuda.empty_cache()
     extra["gemv_multi"] = fused
 
-    # ---------------- 64-layer decode sweep (448 dual GEMVs): separate launches with a
-    # fresh fp16 x per GEMV, and fused launches (q+k+v and gate+up share their x)
+    # ---------------- 64-layer decode sweep (448 dual GEMVs), separate and fused launches
     if not args.no_sweep:
-        mats, xs, ys, total = [], [], [], 0
-        for layer in range(synth.SWEEP_LAYERS):
-            for pi, (name, sn, sk) in enumerate(synth.SWEEP_SHAPES):
-                seed = 10_000 + layer * 16 + pi
-                mats.append((synth.weights_device(0, sn, sk, seed, dev), sn, sk))
-                xs.append(synth.activations_device(1, sk, "f16", seed, dev))
-                ys.append(torch.empty((1, sn), dtype=torch.float32, device=dev))
-                total += sn * synth.row_bytes(0, sk) + sk * 2 + sn * 4
-        torch.cuda.synchronize()
+        extra.update(run_sweeps(torch, R, synth, dev))
 
-        def sweep():
-            for (wm, sn, sk), xx, yy in zip(mats, xs, ys):
-                R.rfp4_gemv(wm, 0, sn, sk, xx, yy)
-
-        sweep()
-        g = torch.cuda.CUDAGraph()
-        s2 = torch.cuda.Stream()
-        s2.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s2):
-            sweep()
-        torch.cuda.current_stream().wait_stream(s2)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=s2):
-            sweep()
-        g.replay()
-        torch.cuda.synchronize()
-        settle_graph(torch, g, 0.3)
-        reps = 5
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        sweep_ms = (time.perf_counter() - t0) * 1e3 / reps
-        extra["sweep_64_layers"] = {"GB/s": round(total / (sweep_ms * 1e-3) / 1e9, 1), "bytes": total,
-                                    "ms_per_sweep": round(sweep_ms, 3), "launches": len(mats),
-                                    "tokens_per_s_equivalent": round(1e3 / sweep_ms, 1)}
-        log(f"sweep: {sweep_ms:.3f} ms -> {extra['sweep_64_layers']['GB/s']:.0f} GB/s")
-
-        # fused: per layer one launch for q+k+v (shared x), o, gate+up (shared x), down
-        nsh = len(synth.SWEEP_SHAPES)
-        groups = [[0, 1, 2], [3], [4, 5], [6]]
-        fcalls, ftotal = [], 0
-        for layer in range(synth.SWEEP_LAYERS):
-            for gidx in groups:
-                ws_ = [mats[layer * nsh + j][0] for j in gidx]
-                ns_ = [mats[layer * nsh + j][1] for j in gidx]
-                kk = mats[layer * nsh + gidx[0]][2]
-                xx = xs[layer * nsh + gidx[0]]
-                yy = [ys[layer * nsh + j] for j in gidx]
-                fcalls.append((ws_, ns_, kk, xx, yy))
-                ftotal += sum(n * synth.row_bytes(0, kk) for n in ns_) + kk * 2 + sum(ns_) * 4
-
-        def fsweep():
-            for ws_, ns_, kk, xx, yy in fcalls:
-                R.rfp4_gemv_multi(ws_, 0, ns_, kk, xx, yy)
-
-        fsweep()
-        g2 = torch.cuda.CUDAGraph()
-        s3 = torch.cuda.Stream()
-        s3.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s3):
-            fsweep()
-        torch.cuda.current_stream().wait_stream(s3)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g2, stream=s3):
-            fsweep()
-        g2.replay()
-        torch.cuda.synchronize()
-        settle_graph(torch, g2, 0.3)
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g2.replay()
-        torch.cuda.synchronize()
-        fsweep_ms = (time.perf_counter() - t0) * 1e3 / reps
-        extra["sweep_64_layers_fused"] = {"GB/s": round(ftotal / (fsweep_ms * 1e-3) / 1e9, 1), "bytes": ftotal,
-                                          "ms_per_sweep": round(fsweep_ms, 3), "launches": len(fcalls),
-                                          "tokens_per_s_equivalent": round(1e3 / fsweep_ms, 1)}
-        log(f"sweep fused: {fsweep_ms:.3f} ms -> {extra['sweep_64_layers_fused']['GB/s']:.0f} GB/s")
-        del mats, xs, ys, fcalls, g, g2
-        torch.cuda.empty_cache()
-
-    # ---------------- CPU baseline: the fp64 oracle on the host
+    # ---------------- CPU baseline: the fp64 oracle on the host, per workload
     cpu = None
     if not args.no_cpu:
-        import oracle.rfp4_oracle as O
-
-        try:
-            from threadpoolctl import threadpool_info
-
-            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:
-            blas_threads = 1
-        xh = x_host.double().numpy()
-        reps, t_cpu = 0, 0.0
-        while t_cpu < 10.0 and reps < 64:  # about 10 s of oracle work
-            t0 = time.perf_counter()
-            O.gemv(w_host, layout, n, k, xh)
-            t_cpu += time.perf_counter() - t0
-            reps += 1
-        cpu = {"value": round(alg_bytes * reps / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-               "kind": "oracle",
-               "sample": f"{reps} full up-projection GEMVs (dequant + fp64 matvec + |w||x| denominator), "
-                         f"{t_cpu:.1f} s; host has {len(os.sched_getaffinity(0))} usable cores"}
-        log(f"cpu oracle: {cpu['value']} GB/s over {reps} reps")
+        cpu = cpu_baseline(synth, w_host, x_host, layout, n, k, alg_bytes)
+        log(f"cpu oracle: {cpu['value']} GB/s (up-projection); per workload: "
+            + ", ".join(f"{kk} {v['value']} {v['unit']}" for kk, v in cpu["per_workload"].items()))
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -543,7 +711,18 @@ def main():
                    "rotation_copies": nc, "timing": "HIP graph of K launches, wall clock"},
         "roofline": roofline, "cpu_baseline": cpu, "gemm": gemm, "extra": extra,
     }
+    status = 0
+    if args.guard:
+        ok, report = guard(result, args.guard)
+        result["guard"] = {"reference": os.path.relpath(args.guard, ROOT), "ok": ok, "tolerance": 0.10,
+                           "entries": report}
+        if not ok:
+            log("guard: regression of more than 10 % against " + args.guard + ": "
+                + ", ".join(kk for kk, v in report.items() if v["regression"]))
+            status = 3
     print(json.dumps(result), flush=True)
+    if status:
+        sys.exit(status)
 
 
 if __name__ == "__main__":
