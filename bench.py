@@ -188,10 +188,9 @@ def bench_gemv_graph(torch, R, copies, layout, n, k, x, y, steps, warmup):
 READ_UNROLL, READ_WGS_PER_CU = 1, 8  # the fastest launch shape of a sweep on MI355X
 
 
-def read_ceiling(torch, copies, w_bytes, dev):
-    """Plain streaming read (librfp4_bench.so) of the rotated weight copies (the bytes the
-    headline GEMV reads, one 50 MB copy per launch) and of one 800 MiB buffer: the HBM
-    read rate a kernel of that size reaches, for comparison with the GEMV."""
+def bench_reader(torch, dev):
+    """read(t, nbytes): one launch of the plain streaming read kernel (librfp4_bench.so)
+    over the first nbytes of device tensor t, on the current stream."""
     import ctypes
 
     lib_path = os.path.join(ROOT, "gemm_rfp4_block_amd", "_lib", "librfp4_bench.so")
@@ -207,6 +206,14 @@ def read_ceiling(torch, copies, w_bytes, dev):
         if st != 0:
             raise RuntimeError(f"rfp4bench_read failed: {st}")
 
+    return read
+
+
+def read_ceiling(torch, copies, w_bytes, dev):
+    """Plain streaming read (librfp4_bench.so) of the rotated weight copies (the bytes the
+    headline GEMV reads, one 50 MB copy per launch) and of one 800 MiB buffer: the HBM
+    read rate a kernel of that size reaches, for comparison with the GEMV."""
+    read = bench_reader(torch, dev)
     nc = len(copies)
     fn = lambda i: read(copies[i % nc], w_bytes)
     warm_up(torch, fn, 0.1)
@@ -291,17 +298,17 @@ def cpu_baseline(synth, w_host, x_host, layout, n, k, alg_bytes):
     per = {}
     tw, tx, tcfg = synth.gemv_inputs("tiny")
     txh = tx.double().numpy()
-    reps, t = timed(lambda: O.gemv(tw, tcfg["layout"], tcfg["n"], tcfg["k"], txh), 0.5, 2000)
+    reps, t = timed(lambda: O.gemv(tw, tcfg["layout"], tcfg["n"], tcfg["k"], txh), 1.0, 4000)
     tb = tw.size + tcfg["k"] * 2 + tcfg["n"] * 4
     per["tiny_gemv"] = {"value": round(tb * reps / t / 1e9, 4), "unit": "GB/s", "reps": reps, "s": round(t, 2)}
     xh = x_host.double().numpy()
-    reps, t = timed(lambda: O.gemv(w_host, layout, n, k, xh), 4.0, 16)
+    reps, t = timed(lambda: O.gemv(w_host, layout, n, k, xh), 8.0, 40)
     up = {"value": round(alg_bytes * reps / t / 1e9, 4), "unit": "GB/s", "reps": reps, "s": round(t, 2)}
     per["up_gemv"] = up
     dw, dx, dcfg = synth.gemv_inputs("down")
     for b in (1, 2, 4, 8):
         xb = dx[:b].double().numpy()
-        reps, t = timed(lambda: O.gemv(dw, dcfg["layout"], dcfg["n"], dcfg["k"], xb), 0.0, 1)
+        reps, t = timed(lambda: O.gemv(dw, dcfg["layout"], dcfg["n"], dcfg["k"], xb), 1.0, 8)
         bts = dw.size + b * dcfg["k"] * 2 + b * dcfg["n"] * 4
         per[f"down_gemv_b{b}"] = {"value": round(bts * reps / t / 1e9, 4), "unit": "GB/s", "reps": reps,
                                   "s": round(t, 2)}
@@ -315,7 +322,7 @@ def cpu_baseline(synth, w_host, x_host, layout, n, k, alg_bytes):
     return {"value": up["value"], "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
             "host_cores": len(os.sched_getaffinity(0)),
             "sample": f"up-projection GEMV (17408 x 5120 dual, fp16 x, batch 1) x {up['reps']} in {up['s']} s; "
-                      f"per_workload: the tiny GEMV repeated, the down-projection GEMV once per batch, "
+                      f"per_workload: the tiny GEMV repeated, the down-projection GEMV (5120 x 17408 fast, bf16 x) for about a second per batch, "
                       f"the full 2048 x 17408 x 5120 prefill GEMM once; {total_s:.1f} s of oracle work in all",
             "per_workload": per}
 
@@ -499,12 +506,17 @@ def main():
         nc = len(copies)
         for i in range(max(args.steps, 24)):
             R.rfp4_gemv(copies[i % nc], layout, n, k, x, y)
+        # the read-ceiling kernel over the same copies (its own rows in the counter output)
+        read = bench_reader(torch, dev)
+        for i in range(max(args.steps, 24)):
+            read(copies[i % nc], w_bytes)
         src = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"pmc mode done: {max(args.steps, 24)} gemv launches of {alg_bytes} algorithmic bytes, "
+        log(f"pmc mode done: {max(args.steps, 24)} gemv launches of {alg_bytes} algorithmic bytes and as "
+            f"many streaming reads of {w_bytes} bytes, "
             f"one copy of {src.numel()} bytes")
         return
 
