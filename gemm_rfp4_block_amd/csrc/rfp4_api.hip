@@ -22,6 +22,10 @@ constexpr int64_t kMaxElems = int64_t(1) << 39;  // elements of A or C (2^40 byt
 bool layout_ok(int layout) { return layout == RFP4_DUAL || layout == RFP4_FAST; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// Activations, A, y and C need only 4-byte alignment: the kernels store outputs one
+// element at a time, and gfx950's global vector loads take any address (an activation
+// row that is not 16-byte aligned costs load cycles, not correctness).
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Shape and alignment of the packed weight matrix, shared by every device entry point.
 // Rows may have any length (k % 32 == 0): the kernels read blocks at any byte offset.
@@ -132,7 +136,7 @@ rfp4_status rfp4_gemv_multi_ex(int count, const void* const* w, const int64_t* n
     if (st != RFP4_OK) return st;
     if (ldy[i] < n[i] || ldy[i] > kMaxDim) return RFP4_ERR_SHAPE;
     if (y[i] == nullptr) return RFP4_ERR_NULL;
-    if (!aligned16(y[i])) return RFP4_ERR_UNSUPPORTED;
+    if (!aligned4(y[i])) return RFP4_ERR_UNSUPPORTED;
     rows += n[i];
     parts[i] = rfp4::GemvPart{static_cast<const uint8_t*>(w[i]), n[i], y[i], ldy[i]};
   }
@@ -141,7 +145,7 @@ rfp4_status rfp4_gemv_multi_ex(int count, const void* const* w, const int64_t* n
   if (batch < 1 || batch > 8) return RFP4_ERR_SHAPE;
   if (ldx < k || ldx > kMaxDim) return RFP4_ERR_SHAPE;
   if (x == nullptr) return RFP4_ERR_NULL;
-  if (!aligned16(x) || (ldx % 8) != 0) return RFP4_ERR_UNSUPPORTED;
+  if (!aligned4(x) || (ldx % 2) != 0) return RFP4_ERR_UNSUPPORTED;
   return from_hip(rfp4::launch_gemv(parts, count, layout, k, x, xdtype, static_cast<int>(batch),
                                     ldx, f, static_cast<hipStream_t>(stream)));
 }
@@ -179,8 +183,7 @@ rfp4_status check_gemm(const void* w, int layout, int64_t n, int64_t k, const vo
   if (lda < k || ldc < n || lda > kMaxDim || ldc > kMaxDim) return RFP4_ERR_SHAPE;
   if (lda > kMaxElems / m || ldc > kMaxElems / m) return RFP4_ERR_SHAPE;
   if (a == nullptr || c == nullptr) return RFP4_ERR_NULL;
-  if (!aligned16(a) || !aligned16(c) || (lda % 8) != 0 || (ldc % 8) != 0)
-    return RFP4_ERR_UNSUPPORTED;
+  if (!aligned4(a) || !aligned4(c) || (lda % 2) != 0) return RFP4_ERR_UNSUPPORTED;
   return RFP4_OK;
 }
 }  // namespace

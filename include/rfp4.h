@@ -39,10 +39,13 @@
  *     paths: call rfp4_validate once when the weights are loaded.
  *   - Alignment: W must start on a 16-byte boundary (RFP4_ERR_UNSUPPORTED
  *     otherwise); its rows may have any length, so k is any multiple of 32 and rows
- *     need not start on a 16-byte boundary. Activations and outputs must be 16-byte
- *     aligned with leading dimensions that keep every row 16-byte aligned (every
- *     activation and output row is moved with 16-byte vector accesses; buffers from
- *     a device allocator meet this, slices at odd offsets do not).
+ *     need not start on a 16-byte boundary. The activations x and A and the outputs
+ *     y and C need 4-byte alignment, with an even leading dimension for x and A (every
+ *     16-bit activation row then starts on a 4-byte boundary); any ldy and ldc are
+ *     accepted. Rows that are not 16-byte aligned are read with the same vector loads
+ *     at some cost in load cycles. The dequant outputs and the encoder's buffers keep
+ *     the 16-byte rule stated with those calls (they are written and read with
+ *     16-byte vector accesses).
  *   - Sizes: 1 <= n, m and 32 <= k, with n, m, k <= 2^31 - 1 and W at most 2^40
  *     bytes (RFP4_ERR_SHAPE otherwise); buffers are addressed with 64-bit offsets.
  */
@@ -121,7 +124,7 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  * Options", Option 2): for b < batch and r < n,
  *   y[b * ldy + r] = sum_c weight(r, c) * x[b * ldx + c]
  * with x of dtype xdtype (RFP4_F16 or RFP4_BF16), products formed exactly and summed
- * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx % 8 == 0), ldy >= n.
+ * in fp32, y fp32. 1 <= batch <= 8, ldx >= k (ldx even), ldy >= n.
  * Kernel choice (each sums in its own fp32 order, so the last bits differ between
  * them; rfp4_gemv_multi_ex can force one):
  *   - batch 1: a dot-product kernel; launches with the dual layout, f16 activations,
@@ -167,7 +170,7 @@ RFP4_API rfp4_status rfp4_gemv_multi(int count, const void* const* w, const int6
  *   c[i * ldc + r] = bf16_rne( sum_q a[i * lda + q] * weight(r, q) ),  i < m, r < n
  * i.e. C = A * W^T with A (m x k, bf16, row-major) and C (m x n, bf16, row-major);
  * weight tiles are decoded to bf16 in LDS and multiplied on the matrix cores with
- * fp32 accumulation. lda >= k (lda % 8 == 0), ldc >= n (ldc % 8 == 0), and
+ * fp32 accumulation. lda >= k (lda even), ldc >= n, and
  * m * lda, m * ldc <= 2^39 (RFP4_ERR_SHAPE otherwise).
  * Balance: the columns of C are split between 256 x 256 tiles and trailing strips of
  * 128 x 128 tiles, and the k range of either kind of tile may be split in two or more

@@ -73,7 +73,8 @@ def test_status_strings(L):
 P = ctypes.c_void_p(0x10000)
 P2 = ctypes.c_void_p(0x20000)
 NULL = ctypes.c_void_p(0)
-UNALIGNED = ctypes.c_void_p(0x10008)
+UNALIGNED = ctypes.c_void_p(0x10008)  # breaks W's and the dequant outputs' 16-byte rule
+ODD2 = ctypes.c_void_p(0x10002)  # breaks the 4-byte rule of x, y, A and C
 
 
 def test_dequant_argument_errors(L):
@@ -107,9 +108,9 @@ def test_gemv_argument_errors(L):
     assert f(P, 0, 8, 512, P2, 0, 1, 512, P, 7, NULL) == R.RFP4_ERR_SHAPE  # ldy < n
     assert f(P, 0, -1, 512, P2, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_SHAPE
     assert f(P, 0, 8, 2**31, P2, 0, 1, 2**31, P, 8, NULL) == R.RFP4_ERR_SHAPE
-    assert f(P, 0, 8, 512, P2, 0, 2, 516, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldx % 8
-    assert f(P, 0, 8, 512, UNALIGNED, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
-    assert f(P, 0, 8, 512, P2, 0, 1, 512, UNALIGNED, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 0, 8, 512, P2, 0, 2, 517, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldx odd
+    assert f(P, 0, 8, 512, ODD2, 0, 1, 512, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(P, 0, 8, 512, P2, 0, 1, 512, ODD2, 8, NULL) == R.RFP4_ERR_UNSUPPORTED
     assert f(UNALIGNED, 1, 8, 96, P2, 0, 1, 96, P, 8, NULL) == R.RFP4_ERR_UNSUPPORTED  # W base
     assert f(P, 1, 8, 96, P2, 0, 1, 95, P, 8, NULL) == R.RFP4_ERR_SHAPE  # ldx < k, 51-byte rows
 
@@ -136,7 +137,7 @@ def test_gemv_multi_argument_errors(L):
     # one bad part is reported with that part's error
     assert f(2, arr(vp, [P, NULL]), n2, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_NULL
     assert f(2, w2, arr(i64, [8, 0]), 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_SHAPE
-    assert f(2, w2, n2, 0, 512, P2, 0, 1, 512, arr(vp, [P, UNALIGNED]), l2, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(2, w2, n2, 0, 512, P2, 0, 1, 512, arr(vp, [P, ODD2]), l2, NULL) == R.RFP4_ERR_UNSUPPORTED
     assert f(2, w2, n2, 0, 512, P2, 0, 1, 512, y2, arr(i64, [8, 15]), NULL) == R.RFP4_ERR_SHAPE
     assert f(2, arr(vp, [P, UNALIGNED]), n2, 0, 512, P2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED
     # the total row count must fit in 2^31 - 1
@@ -146,7 +147,7 @@ def test_gemv_multi_argument_errors(L):
     assert f(2, w2, n2, 0, 512, P2, 2, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED  # dtype
     assert f(2, w2, n2, 0, 512, P2, 0, 9, 512, y2, l2, NULL) == R.RFP4_ERR_SHAPE  # batch
     assert f(2, w2, n2, 0, 512, NULL, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_NULL  # x
-    assert f(2, w2, n2, 0, 512, UNALIGNED, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED
+    assert f(2, w2, n2, 0, 512, ODD2, 0, 1, 512, y2, l2, NULL) == R.RFP4_ERR_UNSUPPORTED
 
 
 def test_dequant_bf16_argument_errors(L):
@@ -172,7 +173,7 @@ def test_gemm_dequant_argument_errors(L):
     assert f(NULL, 0, 64, 512, P2, 16, 512, P, 64, NULL, 512, NULL) == R.RFP4_ERR_NULL
     assert f(P, 0, 64, 512, P2, 0, 512, P, 64, P2, 512, NULL) == R.RFP4_ERR_SHAPE  # m = 0
     assert f(P, 0, 64, 512, P2, 16, 512, P, 63, P2, 512, NULL) == R.RFP4_ERR_SHAPE  # ldc < n
-    assert f(P, 0, 64, 512, P2, 16, 516, P, 64, P2, 512, NULL) == R.RFP4_ERR_UNSUPPORTED  # lda % 8
+    assert f(P, 0, 64, 512, P2, 16, 517, P, 64, P2, 512, NULL) == R.RFP4_ERR_UNSUPPORTED  # lda odd
 
 
 def test_gemm_argument_errors(L):
@@ -183,8 +184,9 @@ def test_gemm_argument_errors(L):
     assert f(P, 0, 64, 512, P2, 0, 512, P, 64, NULL) == R.RFP4_ERR_SHAPE  # m = 0
     assert f(P, 0, 64, 512, P2, 16, 511, P, 64, NULL) == R.RFP4_ERR_SHAPE  # lda < k
     assert f(P, 0, 64, 512, P2, 16, 512, P, 63, NULL) == R.RFP4_ERR_SHAPE  # ldc < n
-    assert f(P, 0, 64, 512, P2, 16, 520, P, 68, NULL) == R.RFP4_ERR_UNSUPPORTED  # ldc % 8
-    assert f(P, 0, 64, 512, P2, 16, 516, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED  # lda % 8
+    assert f(P, 0, 64, 512, P2, 16, 520, ODD2, 68, NULL) == R.RFP4_ERR_UNSUPPORTED  # C base
+    assert f(P, 0, 64, 512, ODD2, 16, 520, P, 68, NULL) == R.RFP4_ERR_UNSUPPORTED  # A base
+    assert f(P, 0, 64, 512, P2, 16, 517, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED  # lda odd
     assert f(P, 4, 64, 512, P2, 16, 512, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED
     assert f(UNALIGNED, 0, 64, 96, P2, 16, 96, P, 64, NULL) == R.RFP4_ERR_UNSUPPORTED  # W base
     assert f(P, 0, 64, 96, P2, 16, 95, P, 64, NULL) == R.RFP4_ERR_SHAPE  # lda < k, 54-byte rows
@@ -221,7 +223,7 @@ def test_force_entry_points_check_shapes(L):
         assert L.rfp4_gemv_multi_ex(1, one, n1, 0, 512, P2, 0, 9, 512, y1, ld, fp, NULL) == R.RFP4_ERR_SHAPE
         assert L.rfp4_gemv_multi_ex(1, one, n1, 0, 512, NULL, 0, 1, 512, y1, ld, fp, NULL) == R.RFP4_ERR_NULL
         assert L.rfp4_gemm_ex(P, 0, 64, 512, P2, 16, 511, P, 64, fp, NULL) == R.RFP4_ERR_SHAPE
-        assert L.rfp4_gemm_ex(P, 0, 64, 512, P2, 16, 512, UNALIGNED, 64, fp, NULL) == R.RFP4_ERR_UNSUPPORTED
+        assert L.rfp4_gemm_ex(P, 0, 64, 512, P2, 16, 512, ODD2, 64, fp, NULL) == R.RFP4_ERR_UNSUPPORTED
 
 
 def test_library_sources_read_no_environment_and_never_free_or_synchronize():
