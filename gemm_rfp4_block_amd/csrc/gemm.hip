@@ -29,9 +29,12 @@
 // LDS rows are 64 bf16 (eight 16-byte chunks) with the chunk index XOR-swizzled by the
 // row, so the MFMA fragment reads (32 consecutive rows, one chunk) hit distinct banks.
 //
-// Mapping. Workgroups are dispatched round-robin over the 8 XCDs; with the M-tile index
-// taken as (workgroup id mod M-tiles), the workgroups of an XCD share a few row slabs
-// of A (2.6 MB per 256 rows at K = 5120), which stay in that XCD's L2.
+// Mapping. Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2. The tile order (tile_coords) arranges the XCDs as a grid over (M tiles, N strips)
+// chosen to move the fewest bytes of A and W across the fabric: for the prefill shape
+// 2 x 4, so each XCD works on 4 row slabs of A and a quarter of the weight strips
+// (main-tile fabric reads 265 MB per call, against 430 MB when every XCD streamed all
+// of W; the kernel time is the same either way).
 
 #include <stdlib.h>
 #include <string.h>
@@ -272,6 +275,29 @@ __device__ __forceinline__ void decode_part(const BlockRaw& b, const uint4* tabs
   }
 }
 
+// XCD-aware tile order. Workgroups go to the 8 XCDs round-robin (workgroup b to XCD
+// b mod 8) and each XCD has an L2 of its own. In the plain order (M tile = t mod
+// m_tiles, N tile = t / m_tiles) with 8 M tiles, XCD x holds the slab of A of M tile x
+// and streams every strip of W, so W crosses the fabric eight times. With mg > 0 (the
+// launcher sets it when the tile counts divide), the XCDs form an mg x (8 / mg) grid:
+// XCD x takes the M tiles of group x / (8 / mg) and the N strips of group x mod (8 / mg),
+// in an order that keeps each resident round's tiles on a few slabs and strips, so A
+// crosses the fabric 8 / mg times and W mg times. Every tile is computed the same way
+// whichever workgroup runs it.
+__device__ __forceinline__ void tile_coords(int t, int m_tiles, int tiles, int mg, int& mt, int64_t& nt) {
+  if (mg > 0) {
+    const int ng = 8 / mg;
+    const int x = t & 7;
+    const int j = t >> 3;
+    const int mper = m_tiles / mg;
+    mt = (x / ng) * mper + j % mper;
+    nt = static_cast<int64_t>(x % ng) * ((tiles / m_tiles) / ng) + j / mper;
+  } else {
+    mt = t % m_tiles;
+    nt = t / m_tiles;
+  }
+}
+
 // Workgroup b computes tile t = b mod tiles, i.e. (t mod m_tiles, t / m_tiles), of the
 // region of C whose columns start at n_base, over the part b / tiles of `splits`
 // equal, even-length ranges of the k steps (k / 64 of them, rounded up to an even
@@ -287,7 +313,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
                                                              uint16_t* __restrict__ c,
                                                              int64_t ldc, int m_tiles, int tiles,
                                                              int64_t n_base, int splits,
-                                                             float* __restrict__ partial) {
+                                                             float* __restrict__ partial, int xcd_mg) {
   constexpr int BB = block_bytes(LAYOUT);
   constexpr int TM = Cfg::TM;
   constexpr int TN = Cfg::TN;
@@ -303,8 +329,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(const uint8_t* __re
   const int wn = wid % Cfg::WN;
   const int tile_id = static_cast<int>(blockIdx.x) % tiles;
   const int split = static_cast<int>(blockIdx.x) / tiles;
-  const int m0 = (tile_id % m_tiles) * Cfg::BM;
-  const int64_t n0 = n_base + static_cast<int64_t>(tile_id / m_tiles) * Cfg::BN;
+  int mt;
+  int64_t nt;
+  tile_coords(tile_id, m_tiles, tiles, xcd_mg, mt, nt);
+  const int m0 = mt * Cfg::BM;
+  const int64_t n0 = n_base + nt * Cfg::BN;
   const int64_t rowbytes = static_cast<int64_t>(nb) * BB;
   // BK = 64 = two blocks; steps come in pairs. With KT (k tail: nb not a multiple of
   // four) the last pair reaches past k, and its A chunks and weight blocks beyond k
@@ -720,7 +749,8 @@ template <typename Cfg>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ partial,
                                                           int splits, int tiles, int m_tiles,
                                                           int64_t n_base, int m, int n,
-                                                          uint16_t* __restrict__ c, int64_t ldc) {
+                                                          uint16_t* __restrict__ c, int64_t ldc,
+                                                          int xcd_mg) {
   constexpr int kGroups = Cfg::BM * Cfg::BN / 4;
   const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (g >= static_cast<int64_t>(tiles) * kGroups) return;
@@ -745,8 +775,11 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   const int wid = r / Cfg::TM;
   const int wm = wid / Cfg::WN;
   const int wn = wid % Cfg::WN;
-  const int m0 = (tile % m_tiles) * Cfg::BM;
-  const int64_t n0 = n_base + static_cast<int64_t>(tile / m_tiles) * Cfg::BN;
+  int mt;
+  int64_t nt;
+  tile_coords(tile, m_tiles, tiles, xcd_mg, mt, nt);
+  const int m0 = mt * Cfg::BM;
+  const int64_t n0 = n_base + nt * Cfg::BN;
   const int64_t gn = n0 + wn * Cfg::kWaveN + j * 32 + (lane & 31);
   if (gn >= n) return;
   const int row0 = m0 + wm * Cfg::kWaveM + i * 32 + 8 * e4 + 4 * (lane >> 5);
@@ -795,9 +828,29 @@ hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint
   const int tiles = static_cast<int>(m_tiles * n_tiles);
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(tiles) * splits));
   float* part = splits > 1 ? partial : nullptr;
+  // XCD grouping (tile_coords): the mg x (8 / mg) grid that moves the fewest bytes of A
+  // and W across the fabric, A crossing 8 / mg times and W mg times; 0 (plain order) when
+  // the tile counts do not divide.
+  int mg = 0;
+#ifndef RFP4_GEMM_XCD
+#define RFP4_GEMM_XCD 1
+#endif
+  if (RFP4_GEMM_XCD && tiles % 8 == 0) {
+    const double a_bytes = static_cast<double>(m) * nb * 64;
+    const double w_bytes = static_cast<double>(n_end - n_base) * nb * block_bytes(layout);
+    double best = 0.0;
+    for (int g = 1; g <= 8; g *= 2) {
+      if (m_tiles % g != 0 || n_tiles % (8 / g) != 0) continue;
+      const double cost = a_bytes * (8 / g) + w_bytes * g;
+      if (mg == 0 || cost < best) {
+        best = cost;
+        mg = g;
+      }
+    }
+  }
 #define RFP4_GEMM_LAUNCH(L, KT)                                                     \
   gemm_kernel<L, Cfg, KT><<<grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream>>>( \
-      w, n, nb, a, m, lda, c, ldc, m_tiles, tiles, n_base, splits, part)
+      w, n, nb, a, m, lda, c, ldc, m_tiles, tiles, n_base, splits, part, mg)
   const bool kt = nb % 4 != 0;
   if (layout == kDual) {
     if (kt) RFP4_GEMM_LAUNCH(kDual, true); else RFP4_GEMM_LAUNCH(kDual, false);
@@ -809,7 +862,7 @@ hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint
   if (e != hipSuccess || splits == 1) return e;
   const int64_t groups = static_cast<int64_t>(tiles) * (Cfg::BM * Cfg::BN / 4);
   gemm_reduce_kernel<Cfg><<<dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256), 0, stream>>>(
-      partial, splits, tiles, m_tiles, n_base, m, n, c, ldc);
+      partial, splits, tiles, m_tiles, n_base, m, n, c, ldc, mg);
   return hipGetLastError();
 }
 
