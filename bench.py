@@ -643,11 +643,15 @@ def main():
     if not args.no_gemm:
         wg_host, a_host, gcfg = synth.gemm_inputs("prefill")
         gn, gk, gm = gcfg["n"], gcfg["k"], gcfg["m"]
-        wg = torch.from_numpy(wg_host).to(dev)
+        # rotating weight copies (>= 600 MiB in all), as for the GEMVs: every call reads its
+        # W from HBM rather than from the Infinity Cache
+        gcopies = rotation_copies(torch, R, gcfg["layout"], gn, gk, wg_host, dev, 300)
+        ngc = len(gcopies)
         a = a_host.to(dev)
         c = torch.empty((gm, gn), dtype=torch.bfloat16, device=dev)
-        warm_up(torch, lambda i: R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c))
-        d = stats_us(timed_launches(torch, lambda i: R.rfp4_gemm(wg, gcfg["layout"], gn, gk, a, c), 50))
+        gfn = lambda i: R.rfp4_gemm(gcopies[i % ngc], gcfg["layout"], gn, gk, a, c)
+        warm_up(torch, gfn)
+        d = stats_us(timed_launches(torch, gfn, 50))
         flops = 2.0 * gm * gn * gk
         tf = flops / (d["mean_us"] * 1e-6) / 1e12
         # L2 <-> fabric bytes of one call (its three launches), from the FETCH_SIZE and
@@ -659,14 +663,14 @@ def main():
                 tr = json.load(f)
             if tr.get("source_hash") == source_hash(GEMM_SOURCES):
                 gtraffic = tr.get("bytes_per_call")
-        gemm = {"TFLOP/s": round(tf, 1), "flop": flops, "m": gm, "n": gn, "k": gk,
+        gemm = {"TFLOP/s": round(tf, 1), "flop": flops, "m": gm, "n": gn, "k": gk, "rotation_copies": ngc,
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": gtraffic},
                 **{kk: round(v, 2) for kk, v in d.items()}}
         log(f"gemm: mean {d['mean_us']:.1f} us -> {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
         # the dequantize-then-multiply baseline (bf16 expansion + rocBLAS dense GEMM)
         wbuf = torch.empty((gn, gk), dtype=torch.bfloat16, device=dev)
-        call_fb = lambda i: R.rfp4_gemm_dequant(wg, gcfg["layout"], gn, gk, a, wbuf, c)
+        call_fb = lambda i: R.rfp4_gemm_dequant(gcopies[i % ngc], gcfg["layout"], gn, gk, a, wbuf, c)
         warm_up(torch, call_fb)
         dfb = stats_us(timed_launches(torch, call_fb, 30))
         gemm["dequant_then_dense_baseline"] = {
@@ -674,7 +678,7 @@ def main():
             "what": "rfp4_gemm_dequant: bf16 expansion of W (178 MB written) + rocBLAS dense bf16 GEMM"}
         log(f"gemm dequant+dense baseline: mean {dfb['mean_us']:.1f} us -> "
             f"{gemm['dequant_then_dense_baseline']['TFLOP/s']:.1f} TFLOP/s")
-        del wg, a, c, wbuf
+        del gcopies, a, c, wbuf
         torch.cuda.empty_cache()
 
     # ---------------- fused multi-matrix GEMVs (gate + up, q + k + v), one launch each
