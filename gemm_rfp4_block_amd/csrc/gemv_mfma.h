@@ -113,6 +113,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   constexpr int PU = 4 * P;       // 16-byte activation pieces per unit
   constexpr int XPT = BIG ? 2 * P : P;  // pieces per thread per chunk: batch <= 8 or <= 4
   constexpr int D = R == 2 ? 2 : 3;     // chunks in flight (two with two tiles: registers)
+  // LDS pieces per activation row of a chunk: G units of PU + 1 pieces, plus one piece so
+  // that consecutive rows start 16 bytes apart modulo 256. The 16 lanes of a lane group
+  // read the same piece of up to 8 different rows in one access; with rows a multiple of
+  // 256 bytes apart those reads would all fall on the same four banks.
+  constexpr int XROW = G * (PU + 1) + 1;
   typedef MfmaOps<XT> M;
   extern __shared__ uint4 smem_m[];
 
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   const int col = lane & 15;  // weight row of the tile (B) and activation row (A)
   const int g = 4 * wv + (lane >> 4);  // lane group: unit g of each chunk
   uint4* const lut = smem_m;
-  uint4* const xs = smem_m + 128;  // chunk: batch x G units x (PU + 1) pieces
+  uint4* const xs = smem_m + 128;  // chunk: batch rows of XROW pieces
   mf32x4* const red = reinterpret_cast<mf32x4*>(xs);  // reused after the last chunk
 
   // Tile and part of this workgroup: the grid is tiles x splits, part p of a tile taking
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   }
 
   // Activation chunk t: piece i = (b G + u) PU + p is the 16-byte piece p of unit G t + u
-  // of activation row b, stored at LDS unit (b G + u)(PU + 1) + p; consecutive threads
+  // of activation row b, stored at LDS unit b XROW + u (PU + 1) + p; consecutive threads
   // read consecutive pieces of a row. The loads are clamped to the last piece (and to
   // the row's last unit), so every thread loads XPT pieces in bounds; pieces of units
   // past the row end are zeroed, so the zeroed weights there meet zeros (0 * inf would
@@ -190,7 +195,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = static_cast<int>(threadIdx.x) + j * THREADS;
-      if (i < pieces) xs[(i / PU) * (PU + 1) + i % PU] = c.v[j];
+      if (i < pieces) {
+        const int bu = i / PU;
+        xs[(bu / G) * XROW + (bu % G) * (PU + 1) + i % PU] = c.v[j];
+      }
     }
   };
 
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   // A lane group past the row end holds the row's last unit of weights against zeroed
   // activations, so it adds zeros.
   auto consume = [&](int d) {
-    const uint4* const xu = xs + (xb * G + g) * (PU + 1);
+    const uint4* const xu = xs + xb * XROW + g * (PU + 1);
     auto block = [&](auto b_c) {
       constexpr int B = decltype(b_c)::value;
       uint4 q4[R], t0[R], t1[R];
@@ -389,7 +397,7 @@ inline int mfma_splits(int tiles, int nu, const Force& force) {
 // LDS of a launch: the table plus one activation chunk (or the cross-wavefront sums,
 // if larger).
 inline size_t mfma_lds(int p, int batch, int r) {
-  const size_t chunk = static_cast<size_t>(batch) * 4 * kMfmaWaves * (4 * p + 1) * 16;
+  const size_t chunk = static_cast<size_t>(batch) * (4 * kMfmaWaves * (4 * p + 1) + 1) * 16;
   const size_t red = static_cast<size_t>(r) * kMfmaWaves * 64 * 16;
   return 128 * 16 + (chunk > red ? chunk : red);
 }
