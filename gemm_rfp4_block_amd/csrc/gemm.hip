@@ -835,7 +835,10 @@ hipError_t launch_region(const uint8_t* w, int layout, int n, int nb, const uint
 #ifndef RFP4_GEMM_XCD
 #define RFP4_GEMM_XCD 1
 #endif
-  if (RFP4_GEMM_XCD && tiles % 8 == 0) {
+  // The grid assumes 8 XCDs of 32 CUs (gfx950 as one partition, 256 CUs); a device
+  // exposing another CU count (a partitioned GPU) keeps the plain order, which is equally
+  // correct, only without the locality.
+  if (RFP4_GEMM_XCD && tiles % 8 == 0 && device_cu_count() == 256) {
     const double a_bytes = static_cast<double>(m) * nb * 64;
     const double w_bytes = static_cast<double>(n_end - n_base) * nb * block_bytes(layout);
     double best = 0.0;
