@@ -617,6 +617,34 @@ def test_gemm_dequant_full_size_sampled():
     assert gemm_error(c[:, cols].to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
 
 
+XCD_GRID_CASES = [  # m, n, k, and the XCD grid (M groups) the launcher's byte model picks
+    (256, 4096, 1024, 1),    # one M tile: the XCDs split the N strips only
+    (1024, 4096, 2048, 2),
+    (2048, 2048, 4096, 4),
+    (4096, 2048, 1024, 8),   # A much larger than W: the XCDs split the M tiles only
+]
+
+
+@pytest.mark.parametrize("case", XCD_GRID_CASES, ids=lambda c: "m{}n{}k{}-mg{}".format(*c))
+def test_gemm_xcd_tile_grid(case, force):
+    """Main tiles only, on shapes whose tile counts give each of the XCD grids of the tile
+    order (M groups 1, 2, 4, 8): every output is written (the order is a bijection of the
+    tiles; C starts as NaN) and sampled columns, the first and last of each 256-column
+    strip included, match the oracle."""
+    m, n, k, _ = case
+    force(gemm_plan="main")
+    layout = 0
+    w = synth.weights(np.random.default_rng(4600 + m + n), layout, n, k)
+    a = synth.activations(np.random.default_rng(4601 + k), m, k, "bf16")
+    c = run_gemm(w, layout, n, k, a)
+    assert np.all(np.isfinite(c))
+    rng = np.random.default_rng(4602)
+    strips = np.arange(0, n, 256)
+    cols = np.unique(np.concatenate([rng.choice(n, size=24, replace=False), strips, strips + 255]))
+    c_ref, den = O.gemm_rows(w, layout, n, k, x64(a), cols)
+    assert gemm_error(c[:, cols], c_ref, den) <= TOL
+
+
 def test_gemm_full_size_sampled():
     w, a, cfg = synth.gemm_inputs("prefill")
     n, k, m = cfg["n"], cfg["k"], cfg["m"]
