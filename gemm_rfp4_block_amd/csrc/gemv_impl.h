@@ -28,8 +28,8 @@
 // values (f16: high-byte table plus zero-spread, below; bf16: E4M3 codes and the packed
 // FP8 conversion of rfp4_decode.h) and multiplied with the activations with
 // v_dot2_f32_{f16,bf16}: one fp32 partial sum per 16-weight half, then one fp32 FMA with
-// that half's E4M3 scale. The partial sums of the CL lanes of a row are combined with a
-// butterfly of cross-lane shuffles and the 1/2 of the half-scale is applied at the store.
+// that half's E4M3 scale. The partial sums of the CL lanes of a row are combined with DPP
+// additions and a swizzle (row_sum) and the 1/2 of the half-scale is applied at the store.
 //
 // Activations are staged once per workgroup into LDS when they fit the budget (layout
 // at xs_index), with the first staging loads issued ahead of the first weight units;
@@ -289,6 +289,28 @@ __device__ __forceinline__ void block_dot(uint4 qv, float s0, float s1, bool val
   }
 }
 
+// Sum over the CL = 2^log2cl consecutive lanes of a row, left in every one of them
+// (the same bits in each, since every step adds two equally ordered partial sums): DPP
+// within 16-lane rows (quad_perm swaps of neighbours and of pairs, then the half-row and
+// row mirrors, which pair each lane with one of the other quad or half once those hold
+// equal sums), then a swizzle that exchanges 16-lane rows (xor 16) and, for 64 lanes per
+// row, a shuffle across the halves of the wavefront. The 16-lane steps need no LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum(float v, int log2cl) {
+  if (log2cl >= 1) v = dpp_add<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if (log2cl >= 2) v = dpp_add<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if (log2cl >= 3) v = dpp_add<0x141>(v);  // row_half_mirror
+  if (log2cl >= 4) v = dpp_add<0x140>(v);  // row_mirror
+  // ds_swizzle bit mode: and-mask 0x1F, or-mask 0, xor-mask 0x10 (within 32 lanes)
+  if (log2cl >= 5)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  if (log2cl >= 6) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 // Activation layout in LDS: for activation row b and unit column ud (blocks P*ud ..
 // P*ud + P - 1), 4P consecutive 16-byte units (block-major, then 8-value chunk) plus
 // one padding unit, so a lane reads all of its unit's activations from one base
@@ -498,10 +520,8 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
     unit_block<LAYOUT, XT, BATCH, XLDS, P, 0>(u, xu, xrow, xg, ldx, valid, acc);
     if constexpr (P == 2) unit_block<LAYOUT, XT, BATCH, XLDS, P, 1>(u, xu, xrow, xg, ldx, valid, acc);
     if (++ci == iters) {  // row group complete: reduce over the CL lanes of each row
-      for (int off = cl >> 1; off >= 1; off >>= 1) {
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) acc[b] += __shfl_xor(acc[b], off, 64);
-      }
+      for (int b = 0; b < BATCH; ++b) acc[b] = row_sum(acc[b], log2cl);
       if (c == 0 && row < (single ? n0 : parts.n[mi_c])) {
         float* y = single ? parts.y[0] : parts.y[mi_c];
         const int64_t ldy = single ? parts.ldy[0] : parts.ldy[mi_c];
