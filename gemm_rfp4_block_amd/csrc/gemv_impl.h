@@ -439,7 +439,7 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
   auto load_next = [&](UnitRaw<P>& buf) {
     if (issued < total) {
       const int col = RAGGED ? min(unit_off + c_off, last_off) : unit_off + c_off;
-      load_unit<LAYOUT, P>(gbase + col + lane_off, buf);
+      load_unit<LAYOUT, P>(gbase + static_cast<uint32_t>(col + lane_off), buf);
       advance();
     }
   };
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
   auto load_first = [&](UnitRaw<P>& buf) {
     const bool live = issued < total;  // wave-uniform
     const int col = RAGGED ? min(unit_off + c_off, last_off) : unit_off + c_off;
-    load_unit<LAYOUT, P>(live ? gbase + col + lane_off : w0, buf);
+    load_unit<LAYOUT, P>(live ? gbase + static_cast<uint32_t>(col + lane_off) : w0, buf);
     if (live) advance();
   };
 
