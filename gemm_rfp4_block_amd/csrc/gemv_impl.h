@@ -22,7 +22,9 @@
 // 34, 18, 17) contiguous bytes. The grid is a whole number r of workgroups per CU, all
 // resident (the LDS request pins r), and workgroup w owns an equal contiguous share of
 // the row groups, which its wavefronts take round-robin: every CU gets the same work.
-// Each lane keeps three units in flight.
+// Each lane keeps two or three units in flight (depth_for), with every load issued
+// unconditionally so that the compiler's waits count exactly the units behind the one
+// consumed.
 //
 // Arithmetic. Each block's 32 weights are decoded to f16/bf16 pairs of unscaled codebook
 // values (f16: high-byte table plus zero-spread, below; bf16: E4M3 codes and the packed
@@ -53,10 +55,6 @@ constexpr int kThreadsLarge = 1024;
 constexpr int kXLdsBudget = 40 * 1024;
 constexpr int kXLdsBudgetLarge = 80 * 1024;
 
-// Tuning knob (no effect on results): weight units in flight per lane.
-#ifndef RFP4_GEMV_DEPTH
-#define RFP4_GEMV_DEPTH 3
-#endif
 // Tuning knob (no effect on results): resident wavefronts per CU the launch is sized for.
 #ifndef RFP4_GEMV_WAVES_PER_CU
 #define RFP4_GEMV_WAVES_PER_CU 24
@@ -129,11 +127,15 @@ __device__ __forceinline__ uint32_t wload4(const void* p) {
 }
 
 // Raw bytes of one unit of P consecutive blocks (see the file comment), as words.
+// Once realigned (unit_aligned):
 //   P = 1: d[0..3] = index bytes, d[4] = the scale byte(s) in its low bytes.
 //   P = 2: d[0..7] = bytes 0..31, d[8] = bytes 32..35 (dual) or 32..33 (fast).
+// A unit of a realigned kind (below) holds, between its load and its use, the words
+// from the word boundary below its first byte, and sh = that byte's offset in the word.
 template <int P>
 struct UnitRaw {
   uint32_t d[P == 1 ? 5 : 9];
+  uint32_t sh;
 };
 
 // Units whose size is not a multiple of 4 bytes (single blocks; pairs of 17-byte
@@ -145,35 +147,57 @@ struct UnitRaw {
 // of bytes), so a read never reaches past the word of the matrix's last byte and never
 // crosses into another page.
 template <int LAYOUT, int P>
+constexpr bool unit_realigned() {
+  return (P * block_bytes(LAYOUT)) % 4 != 0 || P == 1;
+}
+
+// The shift is applied where the unit is used (unit_aligned), not here: the loaded
+// words must not be touched until the unit is due, or the compiler waits for this
+// load at once and the units meant to be in flight behind it never are.
+template <int LAYOUT, int P>
 __device__ __forceinline__ void load_unit_realigned(const uint8_t* p, UnitRaw<P>& u) {
   constexpr int NW = P == 1 ? 5 : 9;  // words covering the unit from its word boundary
-  const int sh = static_cast<int>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
   const uint32_t* a = reinterpret_cast<const uint32_t*>(p - sh);
-  uint32_t wv[NW];
   const uint4 v0 = wload16(a);
-  wv[0] = v0.x;
-  wv[1] = v0.y;
-  wv[2] = v0.z;
-  wv[3] = v0.w;
+  u.d[0] = v0.x;
+  u.d[1] = v0.y;
+  u.d[2] = v0.z;
+  u.d[3] = v0.w;
   if constexpr (P == 2) {
     const uint4 v1 = wload16(a + 4);
-    wv[4] = v1.x;
-    wv[5] = v1.y;
-    wv[6] = v1.z;
-    wv[7] = v1.w;
+    u.d[4] = v1.x;
+    u.d[5] = v1.y;
+    u.d[6] = v1.z;
+    u.d[7] = v1.w;
   }
-  wv[NW - 1] = wload4(a + NW - 1);
+  u.d[NW - 1] = wload4(a + NW - 1);
+  u.sh = sh;
+}
+
+// The unit's words realigned to its first byte (a copy for the layouts loaded aligned).
+template <int LAYOUT, int P>
+__device__ __forceinline__ UnitRaw<P> unit_aligned(const UnitRaw<P>& r) {
+  if constexpr (unit_realigned<LAYOUT, P>()) {
+    constexpr int NW = P == 1 ? 5 : 9;
+    UnitRaw<P> u;
 #pragma unroll
-  for (int i = 0; i < NW - 1; ++i) u.d[i] = __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], sh);
-  u.d[NW - 1] = wv[NW - 1] >> (8 * sh);
+    for (int i = 0; i < NW - 1; ++i) u.d[i] = __builtin_amdgcn_alignbyte(r.d[i + 1], r.d[i], r.sh);
+    u.d[NW - 1] = r.d[NW - 1] >> (8 * r.sh);
+    u.sh = 0;
+    return u;
+  } else {
+    return r;
+  }
 }
 
 template <int LAYOUT, int P>
 __device__ __forceinline__ void load_unit(const uint8_t* p, UnitRaw<P>& u) {
-  if constexpr ((P * block_bytes(LAYOUT)) % 4 != 0 || P == 1) {
+  if constexpr (unit_realigned<LAYOUT, P>()) {
     load_unit_realigned<LAYOUT, P>(p, u);
     return;
   }
+  u.sh = 0;
   const uint4 v0 = wload16(p);
   u.d[0] = v0.x;
   u.d[1] = v0.y;
@@ -355,7 +379,7 @@ struct GemvParts {
   int count;
 };
 
-template <int LAYOUT, int XT, int BATCH, bool XLDS, int P, bool RAGGED, int THREADS, int NP>
+template <int LAYOUT, int XT, int BATCH, bool XLDS, int P, bool RAGGED, int THREADS, int NP, int D>
 __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts, int nu, int log2cl,
                                                         int groups,
                                                         const uint16_t* __restrict__ x,
@@ -436,28 +460,21 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
       }
     }
   };
+  // Every load is issued unconditionally (straight-line loads let the compiler wait for
+  // exactly the loads it needs; a load skipped on some path makes its waits count that
+  // path, draining every load in flight): a wavefront with no unit left loads the first
+  // unit of the launch instead (in bounds, one cache line) and never consumes it.
   auto load_next = [&](UnitRaw<P>& buf) {
-    if (issued < total) {
-      const int col = RAGGED ? min(unit_off + c_off, last_off) : unit_off + c_off;
-      load_unit<LAYOUT, P>(gbase + static_cast<uint32_t>(col + lane_off), buf);
-      advance();
-    }
-  };
-  // The first units are issued unconditionally (straight-line loads let the compiler
-  // wait for exactly the loads it needs): a wavefront with no unit left loads the first
-  // unit of the launch instead (in bounds) and never consumes it.
-  auto load_first = [&](UnitRaw<P>& buf) {
     const bool live = issued < total;  // wave-uniform
     const int col = RAGGED ? min(unit_off + c_off, last_off) : unit_off + c_off;
     load_unit<LAYOUT, P>(live ? gbase + static_cast<uint32_t>(col + lane_off) : w0, buf);
     if (live) advance();
   };
 
-  // D units in flight per lane. With the activations staged in LDS, the first
-  // staging loads are issued before the weight units, so the LDS stores wait only for
-  // them (memory counters retire in issue order) while the weight loads stay in flight;
-  // each consumed unit is then replaced by the next one.
-  constexpr int D = RFP4_GEMV_DEPTH;
+  // D units in flight per lane (depth_for). With the activations staged in LDS, the
+  // first staging loads are issued before the weight units, so the LDS stores wait only
+  // for them (memory counters retire in issue order) while the weight loads stay in
+  // flight; each consumed unit is then replaced by the next one.
   UnitRaw<P> rb[D];
   if constexpr (XLDS) {
     const int units = BATCH * 4 * nu * P;  // 16-byte activation units
@@ -484,7 +501,7 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
       const uint4 v3 = *src_of(min(t0 + 3 * THREADS, units - 1));
       if (first) {  // uniform: the first round of every thread
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_first(rb[d]);
+        for (int d = 0; d < D; ++d) load_next(rb[d]);
       }
       if (t0 < units) *dst_of(t0) = v0;
       if (t0 + THREADS < units) *dst_of(t0 + THREADS) = v1;
@@ -517,8 +534,9 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
     const uint4* xu = RAGGED ? xs + ux * (4 * P + 1) : xu0 + ci * (cl * (4 * P + 1));
     const uint16_t* xg = RAGGED ? x + 32 * P * ux : xg0 + ci * (32 * P * cl);
     // Rows past n were loaded from a clamped address; their sums are never stored.
-    unit_block<LAYOUT, XT, BATCH, XLDS, P, 0>(u, xu, xrow, xg, ldx, valid, acc);
-    if constexpr (P == 2) unit_block<LAYOUT, XT, BATCH, XLDS, P, 1>(u, xu, xrow, xg, ldx, valid, acc);
+    const UnitRaw<P> ua = unit_aligned<LAYOUT, P>(u);
+    unit_block<LAYOUT, XT, BATCH, XLDS, P, 0>(ua, xu, xrow, xg, ldx, valid, acc);
+    if constexpr (P == 2) unit_block<LAYOUT, XT, BATCH, XLDS, P, 1>(ua, xu, xrow, xg, ldx, valid, acc);
     if (++ci == iters) {  // row group complete: reduce over the CL lanes of each row
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) acc[b] = row_sum(acc[b], log2cl);
@@ -536,15 +554,20 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParts<NP> parts
     }
   };
 
-  for (int t = 0; t < total; t += D) {
+  // Rounds of D units: while another round follows, each consumed unit is replaced by
+  // a load (of the next unit, or of the launch's first unit once none is left); the
+  // last round loads nothing, so no load outlives the last unit.
+  int t = 0;
+  for (; t + D < total; t += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (d == 0 || t + d < total) {
-        consume(rb[d]);
-        load_next(rb[d]);
-      }
+      consume(rb[d]);
+      load_next(rb[d]);
     }
   }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (t + d < total) consume(rb[d]);
 }
 
 
@@ -618,19 +641,36 @@ inline Plan choose_plan(const GemvPart* parts, int count, int nb, int waves_per_
   return pl;
 }
 
+// Weight units in flight per lane. Every load is issued unconditionally (see the
+// kernel), so a lane whose units do not fill its last round of D loads the launch's
+// first unit in their place: depth 3 when the busiest lane has exactly three units (all
+// issued up front, none repeated), else 2. Measured against depth 3 everywhere (one box,
+// outputs bitwise equal): up-projection 12.55 -> 12.06 us, batch 2 16.55 -> 16.02;
+// 5120 x 17408 fast bf16 batch 1/2 14.78/17.92 -> 14.21/17.41; 5120 x 17408 dual f16
+// 14.66 -> 13.79; while 6144 x 5120 (three units per lane) takes 6.50 us at depth 3 and
+// 6.70 at 2. Batches above 2 (on this kernel only when forced) keep depth 3.
+inline int depth_for(const Plan& pl, int batch) {
+  if (batch > 2) return 3;
+  const int per_wg = pl.threads / 64;
+  const int groups_wg = (pl.groups + pl.wgs - 1) / pl.wgs;  // largest workgroup share
+  const int groups_wave = (groups_wg + per_wg - 1) / per_wg;
+  const int iters = (pl.nu + (1 << pl.log2cl) - 1) >> pl.log2cl;
+  return static_cast<int64_t>(groups_wave) * iters == 3 ? 3 : 2;
+}
+
 // The 1024-thread kernels may need more than 64 KB of dynamic LDS; the limit is raised
 // once per process for each P (an idempotent call, so threads that race repeat it
 // harmlessly).
-template <int LAYOUT, int XT, int BATCH, int NP>
+template <int LAYOUT, int XT, int BATCH, int NP, int D>
 hipError_t raise_lds_limit(int p) {
   static std::atomic<bool> done[2];
   std::atomic<bool>& d = done[p - 1];
   if (d.load(std::memory_order_acquire)) return hipSuccess;
   const void* fns[2] = {
-      reinterpret_cast<const void*>(p == 2 ? &gemv_kernel<LAYOUT, XT, BATCH, true, 2, false, kThreadsLarge, NP>
-                                           : &gemv_kernel<LAYOUT, XT, BATCH, true, 1, false, kThreadsLarge, NP>),
-      reinterpret_cast<const void*>(p == 2 ? &gemv_kernel<LAYOUT, XT, BATCH, true, 2, true, kThreadsLarge, NP>
-                                           : &gemv_kernel<LAYOUT, XT, BATCH, true, 1, true, kThreadsLarge, NP>)};
+      reinterpret_cast<const void*>(p == 2 ? &gemv_kernel<LAYOUT, XT, BATCH, true, 2, false, kThreadsLarge, NP, D>
+                                           : &gemv_kernel<LAYOUT, XT, BATCH, true, 1, false, kThreadsLarge, NP, D>),
+      reinterpret_cast<const void*>(p == 2 ? &gemv_kernel<LAYOUT, XT, BATCH, true, 2, true, kThreadsLarge, NP, D>
+                                           : &gemv_kernel<LAYOUT, XT, BATCH, true, 1, true, kThreadsLarge, NP, D>)};
   for (const void* f : fns) {
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
@@ -690,13 +730,24 @@ hipError_t launch3(const GemvPart* parts, int count, int nb, const uint16_t* x, 
   const size_t pin = (160 * 1024) / (r + 1) + 1024;
   size_t shm = xlds ? (pl.p == 2 ? xbytes2 : xbytes1) : 0;
   if (shm < pin) shm = pin;
+  // Depth 2 exists for batches 1 and 2 only (kD2 is 3 otherwise, so no other kernel is
+  // instantiated).
+  constexpr int kD2 = BATCH <= 2 ? 2 : 3;
+  const bool d2 = depth_for(pl, BATCH) == 2;
   if (large_x && shm > 64 * 1024) {
-    const hipError_t e = raise_lds_limit<LAYOUT, XT, BATCH, NP>(pl.p);
+    const hipError_t e = d2 ? raise_lds_limit<LAYOUT, XT, BATCH, NP, kD2>(pl.p)
+                            : raise_lds_limit<LAYOUT, XT, BATCH, NP, 3>(pl.p);
     if (e != hipSuccess) return e;
   }
-#define RFP4_GEMV_LAUNCH(XL, PP, RG, TH)                                           \
-  gemv_kernel<LAYOUT, XT, BATCH, XL, PP, RG, TH, NP><<<grid, block, shm, stream>>>(\
-      gp, pl.nu, pl.log2cl, pl.groups, x, ldx)
+#define RFP4_GEMV_LAUNCH(XL, PP, RG, TH)                                                     \
+  do {                                                                                       \
+    if (d2)                                                                                  \
+      gemv_kernel<LAYOUT, XT, BATCH, XL, PP, RG, TH, NP, kD2><<<grid, block, shm, stream>>>( \
+          gp, pl.nu, pl.log2cl, pl.groups, x, ldx);                                          \
+    else                                                                                     \
+      gemv_kernel<LAYOUT, XT, BATCH, XL, PP, RG, TH, NP, 3><<<grid, block, shm, stream>>>(   \
+          gp, pl.nu, pl.log2cl, pl.groups, x, ldx);                                          \
+  } while (0)
 #define RFP4_GEMV_LAUNCH_P(XL, RG, TH) \
   if (pl.p == 2) RFP4_GEMV_LAUNCH(XL, 2, RG, TH); else RFP4_GEMV_LAUNCH(XL, 1, RG, TH)
   if (large_x) {

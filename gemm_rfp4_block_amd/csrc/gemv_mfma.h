@@ -229,9 +229,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
       uint4 q4[R], t0[R], t1[R];
 #pragma unroll
       for (int q = 0; q < R; ++q) {
-        q4[q] = unit_qs<LAYOUT, P, B>(rb[q][d]);
+        const UnitRaw<P> ua = unit_aligned<LAYOUT, P>(rb[q][d]);
+        q4[q] = unit_qs<LAYOUT, P, B>(ua);
         uint32_t e0, e1;
-        unit_scale_bytes<LAYOUT, P, B>(rb[q][d], e0, e1);
+        unit_scale_bytes<LAYOUT, P, B>(ua, e0, e1);
         t0[q] = lut[e0];
         t1[q] = LAYOUT == kDual ? lut[e1] : t0[q];
       }

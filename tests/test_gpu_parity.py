@@ -229,6 +229,28 @@ def test_gemv_forced_plan(case, force):
     check_gemv(w, layout, n, k, x, ldy=n + 3)
 
 
+# Tall launches with few lanes per row, so that a wavefront walks two row groups: the
+# busiest lanes then hold more units than one round of loads (depth 2), and lanes with
+# one group fewer end on a round that repeats loads (the launch's first unit, never
+# consumed). Both layouts, both kinds of unit (pairs of 36 / 34 bytes, single blocks
+# realigned from word boundaries), batch 1 and 2.
+ROUNDS = [  # plan, layout, n, k, batch, dtype
+    ("1:8", 0, 65536, 768, 1, "f16"), ("1:8", 1, 65536, 768, 1, "bf16"),
+    ("2:8", 1, 65536, 768, 2, "f16"), ("2:8", 0, 65536, 1536, 2, "bf16"),
+    ("2:4", 1, 30000, 2304, 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", ROUNDS, ids=lambda c: "{}-L{}n{}k{}b{}{}".format(*c))
+def test_gemv_rounds_over_several_row_groups(case, force):
+    plan, layout, n, k, batch, dt = case
+    force(gemv_kernel="dot", gemv_plan=tuple(map(int, plan.split(":"))))
+    rng = np.random.default_rng(5500 + n + k + batch)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.01)
+    x = synth.activations(rng, batch, k, dt)
+    check_gemv(w, layout, n, k, x, ldy=n + 1)
+
+
 MULTI = [  # layout, [n per part], k, batch, dtype
     (0, [17408, 17408], 5120, 1, "f16"),       # gate + up
     (0, [6144, 1024, 1024], 5120, 1, "f16"),   # q, k, v
