@@ -165,11 +165,13 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
 
 // Whether a batch-1 launch takes the tall kernel. A forced kernel (rfp4_force) turns it
 // off (dot product, tiles, no-tall) or on wherever the shape allows (tall). By default,
-// from timings against the dot-product kernel on one machine: k = 5120 only (at k =
-// 6144 it was 7-10 % slower from 12288 rows), at least two tiles per CU, and the
+// from timings against the dot-product kernel on one machine: fused launches of several
+// matrices only (gate + up 21.8 against 22.9 us, q + k + v 6.5 against 6.9; on one matrix
+// the dot-product kernel, which keeps its weight units in flight, was 4-8 % faster at
+// 8192-24576 and 49152 rows and within 1 % elsewhere up to 152064), k = 5120 only (at
+// k = 6144 it was 7-10 % slower from 12288 rows), at least two tiles per CU, and the
 // busiest CU at most 7 % above the average tile count (at 17408 rows, 4.25 tiles per
-// CU, it was 2-5 % slower; with even tile counts from 2 to 8.5 per CU it tied or won
-// by up to 9 %).
+// CU, it was 2-5 % slower).
 inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb, int batch,
                            const Force& force) {
   if (layout != kDual || batch != 1 || (nb != 160 && nb != 192)) return false;
@@ -182,7 +184,7 @@ inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb,
   const int fk = force.gemv_kernel;
   if (fk == RFP4_GEMV_KERNEL_DOT || fk == RFP4_GEMV_KERNEL_TILES || fk == RFP4_GEMV_KERNEL_NO_TALL) return false;
   if (fk == RFP4_GEMV_KERNEL_TALL) return true;
-  if (nb != 160) return false;
+  if (nb != 160 || count < 2) return false;
   const int64_t cus = device_cu_count();
   const int64_t busiest = (tiles + cus - 1) / cus;
   return tiles >= 2 * cus && busiest * cus * 100 <= tiles * 107;

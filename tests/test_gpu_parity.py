@@ -342,7 +342,7 @@ TALL_CASES = [  # row counts of the matrices (one launch), k, activation dtype, 
 @pytest.mark.parametrize("case", TALL_CASES, ids=lambda c: "n{}k{}{}L{}".format("-".join(map(str, c[0])), *c[1:]))
 def test_gemv_tall_forced(case, force):
     """The batch-1 matrix-core kernel for tall launches, forced on wherever the shape
-    allows (RFP4_GEMV_TALL=1), against the oracle; shapes it does not take fall back to
+    allows (the tall kernel forced through rfp4_force), against the oracle; shapes it does not take fall back to
     the dot-product kernel and must stay correct. Weights include 2 % stress blocks
     (extreme codes and scales)."""
     force(gemv_kernel="tall")
@@ -909,9 +909,9 @@ def test_unaligned_rows_gemm_dequant(case):
 
 
 # ------------------------------------------------------------------ GEMV on the matrix cores
-# Both GEMV kernels are checked at every batch by forcing the path: RFP4_GEMV_MFMA=1 runs
-# the matrix-core kernel (16-row tiles, table decode, k split over the wavefronts of a
-# workgroup), =0 the dot-product kernel. Cases cover ragged row counts, odd block counts
+# Both GEMV kernels are checked at every batch by forcing the path (rfp4_force): "tiles"
+# runs the matrix-core kernel (16-row tiles, table decode, k split over the wavefronts of
+# a workgroup), "dot" the dot-product kernel. Cases cover ragged row counts, odd block counts
 # (single-block units), rows that are not 16-byte multiples, activations staged in LDS and
 # read from global memory (long rows, large batches), every wavefront count, and fused
 # launches.
@@ -1144,14 +1144,13 @@ def test_gemv_split_two_streams(force):
             assert torch.equal(ys[s][rep], ys[s][0])
 
 
-@pytest.mark.parametrize("mode,batch", [("0", 1), ("", 1), ("1", 4), ("1", 8)])
+@pytest.mark.parametrize("mode,batch", [("dot", 1), ("tall", 1), ("tiles", 4), ("tiles", 8)])
 def test_gemv_vocab_rows_sampled(mode, batch, force):
     """A vocabulary-sized matrix (152064 x 5120 dual, 438 MB packed: the decode LM head)
-    on each kernel (batch 1: the dot-product kernel forced, and the default, the tall
-    matrix-core kernel), checked on a seeded sample of rows that includes the first and
-    the last."""
-    if mode:
-        force(gemv_kernel={"0": "dot", "1": "tiles"}[mode])
+    on each kernel (batch 1: the dot-product kernel, the default for one matrix, and the
+    tall matrix-core kernel; batches 4 and 8 on the matrix-core tiles), checked on a
+    seeded sample of rows that includes the first and the last."""
+    force(gemv_kernel=mode)
     layout, n, k = 0, 152064, 5120
     rng = np.random.default_rng(9700 + batch)
     w = synth.weights(rng, layout, n, k)
