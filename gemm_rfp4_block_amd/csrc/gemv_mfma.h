@@ -9,19 +9,20 @@
 // on large launches. Lane l of a wavefront serves
 // as B-operand lane for weight row l % 16 and as A-operand lane for activation row
 // l % 16 (rows beyond the batch read a clamped, finite row whose results are never
-// stored); the lane group g = 4 w + l / 16 (w the wavefront) takes units g, g + 16,
-// g + 32, ... of the row (a unit is P = 1 or 2 consecutive blocks, loaded as in the
-// dot-product kernel). The sum over k is order free, so each MFMA adds, for every lane
-// group, 8 consecutive weights of that lane's own unit against the matching 8
-// activations: block j gives four MFMA steps s = 0..3 over weights 8s .. 8s+7 (low
+// stored); the lane group g = 4 w + l / 16 (w the wavefront) multiplies units g, g + 16,
+// g + 32, ... of the row (a unit is P = 1 or 2 consecutive blocks). The weights are
+// loaded along rows and handed to these lanes through an LDS stage per chunk (below).
+// The sum over k is order free, so each MFMA adds, for every lane group, 8 consecutive
+// weights of that lane's own unit against the matching 8 activations: block j gives four MFMA steps s = 0..3 over weights 8s .. 8s+7 (low
 // nibbles of qs words 0, 1 / 2, 3, then the high nibbles), and the activations of step
 // s are the 16-byte piece s of the block.
 //
 // Activations. The 16 lane groups consume the units of a row in chunks of 16 (chunk
 // t = units 16t .. 16t + 15). Each chunk's activations, for all batch rows, are staged
-// in LDS just before it is multiplied; the loads are issued three chunks ahead into
-// registers, together with the weights of the same chunk, so that the staging waits
-// only for loads that are due anyway. Per chunk the workgroup reads batch x 16 units of
+// in LDS just before it is multiplied, and so are its weights (each lane stores the
+// unit it loaded and reads back the unit it multiplies); the loads are issued three
+// chunks ahead into registers, activations and weights of a chunk together, so that
+// the staging waits only for loads that are due anyway. Per chunk the workgroup reads batch x 16 units of
 // activations from the L2; staging the whole activation matrix up front, or having
 // every lane read its activations from global memory, measured 1.2 to 1.6 times slower.
 // Four wavefronts per workgroup measured faster than 8 or 16 on every decode shape
@@ -128,6 +129,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   uint4* const lut = smem_m;
   uint4* const xs = smem_m + 128;  // chunk: batch rows of XROW pieces
   mf32x4* const red = reinterpret_cast<mf32x4*>(xs);  // reused after the last chunk
+  // Weight stage of a chunk, after its activations: the (realigned) words of unit u of
+  // tile row r in planes of 16-byte slots (words 0-3, and 4-7 for pairs) and 4-byte slots
+  // (the last word), slot q * 256 + u * 16 + (r ^ u) for tile q. The 16 lanes that store
+  // one row's units and the 16 lanes that read one unit of every row both touch 16
+  // distinct slot positions modulo 16, i.e. distinct banks.
+  uint4* const ws_a = xs + batch * XROW;
+  uint4* const ws_b = ws_a + R * 256;  // pairs only
+  uint32_t* const ws_c = reinterpret_cast<uint32_t*>(ws_a + R * 256 * (P == 2 ? 2 : 1));
 
   // Tile and part of this workgroup: the grid is tiles x splits, part p of a tile taking
   // its chunks [p T_all / splits, (p + 1) T_all / splits) (the plan keeps splits <= T_all).
@@ -140,18 +149,26 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   const int n_part = NP > 1 ? parts.n[mi] : parts.n[0];
   const int r0 = (tile - (NP > 1 ? parts.gbeg[mi] : 0)) * 16 * R;
   const int64_t rowbytes = static_cast<int64_t>(nu) * UB;
+  // Weight loads run along rows: lane l of wavefront w loads unit l % 16 of the chunk
+  // from tile row 4 w + l / 16, so each load instruction reads 16 consecutive units of
+  // four rows (the MFMA lane of a (row, unit) pair holds one unit of each of 16 rows,
+  // which would make every instruction touch 16 rows). The units reach their MFMA lanes
+  // through the weight stage in LDS.
+  static_assert(W == 4, "the weight stage maps 4 wavefronts x 4 lane groups to 16 rows and 16 units");
+  const int lrow = 4 * wv + (lane >> 4);
+  const int lunit = lane & 15;
   const uint8_t* wrow[R];
 #pragma unroll
   for (int q = 0; q < R; ++q)
-    wrow[q] = (NP > 1 ? parts.w[mi] : parts.w[0]) + static_cast<int64_t>(min(r0 + 16 * q + col, n_part - 1)) * rowbytes;
+    wrow[q] = (NP > 1 ? parts.w[mi] : parts.w[0]) + static_cast<int64_t>(min(r0 + 16 * q + lrow, n_part - 1)) * rowbytes;
 
-  // Chunk c covers units G c .. G c + G - 1 of every row: lane group g takes unit
+  // Chunk c covers units G c .. G c + G - 1 of every row: lane group g multiplies unit
   // G c + g (past the row end the address is clamped). This part's chunks are
   // c = t_off + t, t < T.
   const int T_all = (nu + G - 1) / G;
   const int t_off = part * T_all / splits;
   const int T = (part + 1) * T_all / splits - t_off;
-  auto unit_ptr = [&](int q, int t) { return wrow[q] + static_cast<int64_t>(min(G * (t_off + t) + g, nu - 1)) * UB; };
+  auto unit_ptr = [&](int q, int t) { return wrow[q] + static_cast<int64_t>(min(G * (t_off + t) + lunit, nu - 1)) * UB; };
 
   // Decode table (threads 0..127).
   if (threadIdx.x < 128) {
@@ -202,9 +219,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     }
   };
 
-  // Three chunks in flight: the activations of chunk t are loaded just before its
-  // weights, so the LDS store of chunk t waits for exactly those loads and leaves the
-  // weights of chunk t (and later) in flight.
+  // Three chunks in flight: the activations and weights of chunk t are loaded together,
+  // so the LDS stores of chunk t wait for exactly those loads and leave the later chunks
+  // in flight.
   XChunk xr[D];
   UnitRaw<P> rb[R][D];
 #pragma unroll
@@ -215,6 +232,44 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     for (int q = 0; q < R; ++q) load_unit<LAYOUT, P>(unit_ptr(q, tc), rb[q][d]);
   }
 
+  auto w_store = [&](int d) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const UnitRaw<P> ua = unit_aligned<LAYOUT, P>(rb[q][d]);
+      const int sl = q * 256 + lunit * 16 + (lrow ^ lunit);
+      ws_a[sl] = uint4{ua.d[0], ua.d[1], ua.d[2], ua.d[3]};
+      if constexpr (P == 2) {
+        ws_b[sl] = uint4{ua.d[4], ua.d[5], ua.d[6], ua.d[7]};
+        ws_c[sl] = ua.d[8];
+      } else {
+        ws_c[sl] = ua.d[4];
+      }
+    }
+  };
+  // The unit this lane multiplies (tile row col, unit g of the chunk), from the stage.
+  auto w_read = [&](int q) {
+    const int sl = q * 256 + g * 16 + (col ^ g);
+    UnitRaw<P> u;
+    const uint4 a = ws_a[sl];
+    u.d[0] = a.x;
+    u.d[1] = a.y;
+    u.d[2] = a.z;
+    u.d[3] = a.w;
+    if constexpr (P == 2) {
+      const uint4 b = ws_b[sl];
+      u.d[4] = b.x;
+      u.d[5] = b.y;
+      u.d[6] = b.z;
+      u.d[7] = b.w;
+      u.d[8] = ws_c[sl];
+    } else {
+      u.d[4] = ws_c[sl];
+    }
+    u.sh = 0;
+    return u;
+  };
+
+
   const int xb = min(col, batch - 1);  // activation row of this A lane (clamped)
   mf32x4 acc[R];
 #pragma unroll
@@ -223,16 +278,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   // A lane group past the row end holds the row's last unit of weights against zeroed
   // activations, so it adds zeros.
   auto consume = [&](int d) {
+    (void)d;  // the chunk's weights are in the stage, its activations in xs
     const uint4* const xu = xs + xb * XROW + g * (PU + 1);
+    UnitRaw<P> ua[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) ua[q] = w_read(q);
     auto block = [&](auto b_c) {
       constexpr int B = decltype(b_c)::value;
       uint4 q4[R], t0[R], t1[R];
 #pragma unroll
       for (int q = 0; q < R; ++q) {
-        const UnitRaw<P> ua = unit_aligned<LAYOUT, P>(rb[q][d]);
-        q4[q] = unit_qs<LAYOUT, P, B>(ua);
+        q4[q] = unit_qs<LAYOUT, P, B>(ua[q]);
         uint32_t e0, e1;
-        unit_scale_bytes<LAYOUT, P, B>(ua, e0, e1);
+        unit_scale_bytes<LAYOUT, P, B>(ua[q], e0, e1);
         t0[q] = lut[e0];
         t1[q] = LAYOUT == kDual ? lut[e1] : t0[q];
       }
@@ -272,6 +330,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     for (int d = 0; d < D; ++d) {
       if (t + d > 0) __syncthreads();
       x_store(xr[d]);
+      w_store(d);
       __syncthreads();
       consume(d);
       const int tn = min(t + d + D, T - 1);
@@ -285,6 +344,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     if (t + d < T) {
       if (t + d > 0) __syncthreads();
       x_store(xr[d]);
+      w_store(d);
       __syncthreads();
       consume(d);
     }
@@ -395,10 +455,11 @@ inline int mfma_splits(int tiles, int nu, const Force& force) {
   return s;
 }
 
-// LDS of a launch: the table plus one activation chunk (or the cross-wavefront sums,
-// if larger).
+// LDS of a launch: the table plus one activation chunk and its weight stage (or the
+// cross-wavefront sums, if larger).
 inline size_t mfma_lds(int p, int batch, int r) {
-  const size_t chunk = static_cast<size_t>(batch) * (4 * kMfmaWaves * (4 * p + 1) + 1) * 16;
+  const size_t chunk = static_cast<size_t>(batch) * (4 * kMfmaWaves * (4 * p + 1) + 1) * 16 +
+                       static_cast<size_t>(r) * 256 * (p == 2 ? 36 : 20);
   const size_t red = static_cast<size_t>(r) * kMfmaWaves * 64 * 16;
   return 128 * 16 + (chunk > red ? chunk : red);
 }
@@ -468,25 +529,26 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
                 : launch_mfma_p<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream);
 }
 
-// Matrix-core path for the launches where it is faster. Measured on the decode shapes
-// (graph-replayed launches over rotating weight copies, one machine): the dot-product
-// kernel wins at batch 1 (12.5 against 14.7 us at 17408 x 5120: its decode needs no
-// table, no staging and no cross-wave reduction) and still at batch 2 on long rows or
-// many rows (17408 x 5120 16.15 / 16.84 us, 5120 x 17408 19.59 / 20.05, 5120 x 6144
-// 9.63 / 10.12, dot-product / matrix cores) but not on 6144 x 5120 (9.24 / 9.02), fused
-// q + k + v (9.75 / 10.15 with the dot-product kernel) or fused gate + up, 34816 rows
-// (28.0 / 29.9), where the matrix-core tiles fill the CUs evenly; from batch 3 the
-// matrix cores win on all of these (their decode does not grow with the batch).
+// Matrix-core path for the launches where it is faster. Measured (graph-replayed
+// launches over rotating weight copies, one machine, dot-product / matrix cores, us):
+// the dot-product kernel wins at batch 1 (its decode needs no table, no staging and no
+// cross-wave reduction) and at batch 2 on one matrix (17408 x 5120 16.31 / 16.78,
+// 5120 x 17408 17.51 / 19.29, 5120 x 6144 9.46 / 9.85, 1024 x 5120 4.75 / 6.60,
+// 152064 x 5120 92.3 / 100.7, 49152 x 5120 33.5 / 35.4; the matrix cores were ahead by at
+// most 3 % at 3072, 4096 and 34816 rows) and on fused launches below 32768 rows (q + k + v
+// 8.83 / 8.96, k + v 5.92 / 6.31), not on fused gate + up (27.27 / 26.84). From batch 3
+// the matrix cores win (their decode does not grow with the batch), except on one
+// matrix of at most 1024 short rows up to batch 6 (1024 x 5120 batch 3/4/6 5.63 / 6.74,
+// 6.19 / 6.80, 7.25 / 7.49; at batch 8 8.75 / 7.66, and from 2048 rows the tiles lead).
 // A forced kernel (rfp4_force) replaces the choice.
 inline bool use_mfma(const GemvPart* parts, int count, int nb, int batch, const Force& force) {
   if (force.gemv_kernel == RFP4_GEMV_KERNEL_DOT) return false;
   if (force.gemv_kernel == RFP4_GEMV_KERNEL_TILES) return true;
   if (batch < 2) return false;
-  if (batch == 2) {
-    int64_t rows = 0;
-    for (int i = 0; i < count; ++i) rows += parts[i].n;
-    if ((nb >= 192 || rows >= 16384) && rows < 32768) return false;
-  }
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) rows += parts[i].n;
+  if (batch == 2) return count > 1 && rows >= 32768;
+  if (batch <= 6 && count == 1 && rows <= 1024 && nb <= 192) return false;
   return true;
 }
 
