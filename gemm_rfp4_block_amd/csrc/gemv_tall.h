@@ -8,8 +8,10 @@
 // differently.
 //
 // Tiles of 16 rows, one per workgroup of four wavefronts. Lane l of wavefront w holds
-// row l % 16 of the tile and belongs to lane group g = l / 16; it streams the units
-// (pairs of blocks, 36 bytes) w * 4 + g, + 16, + 32, ... of its row, three in flight.
+// row l % 16 of the tile and belongs to lane group g = l / 16; it multiplies the units
+// (pairs of blocks, 36 bytes) w * 4 + g, + 16, + 32, ... of its row. The units are
+// loaded along rows by other lanes, three steps in flight, and handed over through LDS
+// (see the kernel).
 // Each 32-bit word of codes (8 weights: 4 of the first half, 4 of the second) is
 // decoded on the VALU into unscaled f16 codebook values (the high-byte table of the
 // dot-product kernel) and is the B fragment of one v_mfma_f32_16x16x32_f16; the eight
@@ -83,10 +85,10 @@ struct TallParts {
   int count;
 };
 
-template <int NUL, bool SINGLE>
+template <int NUL, bool SINGLE, bool STAGED>
 __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
                                                         const uint16_t* __restrict__ x) {
-  extern __shared__ uint4 tall_xs[];  // 8 pieces per block, then 8 zero pieces
+  extern __shared__ uint4 tall_xs[];  // 8 pieces per block, 8 zero pieces, the weight stage
   constexpr int kNb = 32 * NUL;       // blocks per row
   constexpr int kPieces = 8 * kNb;
   constexpr int64_t kRowBytes = 16 * NUL * 36;
@@ -98,7 +100,37 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
     while (mi + 1 < parts.count && static_cast<int>(blockIdx.x) >= parts.tbeg[mi + 1]) ++mi;
   }
   const int row = (static_cast<int>(blockIdx.x) - parts.tbeg[mi]) * 16 + nl;
-  const uint8_t* wr = parts.w[mi] + row * kRowBytes;
+  // STAGED: weight loads run along rows: lane l of wavefront w loads unit 16 t + l % 16
+  // of tile row 4 w + l / 16 (16 consecutive units of 4 rows per load instruction, where
+  // the lanes' own units span 16 rows), and each unit reaches the lane that multiplies it
+  // (row l % 16, unit 16 t + 4 w + l / 16) through a double-buffered LDS stage: planes of
+  // 16-byte slots (words 0-3, 4-7) and 4-byte slots (word 8) at u * 16 + (r ^ u) for row
+  // r and unit u of the step, bank-conflict free for the storing and the reading lanes.
+  // One barrier per step suffices: a buffer is stored again two steps later, and every
+  // lane has finished reading it before it reaches the barrier in between. Otherwise each
+  // lane loads the units it multiplies.
+  const uint8_t* wr = STAGED ? parts.w[mi] + ((static_cast<int>(blockIdx.x) - parts.tbeg[mi]) * 16 + 4 * wv + g) * kRowBytes
+                             : parts.w[mi] + row * kRowBytes;
+  const int u_load = STAGED ? nl : wv * 4 + g;  // unit of each step this lane loads
+  uint4* const st_a = tall_xs + kPieces + 8;  // two buffers of 256 + 256 + 64 pieces
+  auto stage_put = [&](int buf, const TallUnit& u) {
+    const int sl = nl * 16 + ((4 * wv + g) ^ nl);
+    uint4* const b = st_a + buf * 576;
+    b[sl] = uint4{u.d[0], u.d[1], u.d[2], u.d[3]};
+    b[256 + sl] = uint4{u.d[4], u.d[5], u.d[6], u.d[7]};
+    reinterpret_cast<uint32_t*>(b + 512)[sl] = u.d[8];
+  };
+  auto stage_get = [&](int buf) {
+    const int un = 4 * wv + g;
+    const int sl = un * 16 + (nl ^ un);
+    const uint4* const b = st_a + buf * 576;
+    const uint4 a = b[sl], c = b[256 + sl];
+    TallUnit u;
+    u.d[0] = a.x; u.d[1] = a.y; u.d[2] = a.z; u.d[3] = a.w;
+    u.d[4] = c.x; u.d[5] = c.y; u.d[6] = c.z; u.d[7] = c.w;
+    u.d[8] = reinterpret_cast<const uint32_t*>(b + 512)[sl];
+    return u;
+  };
 
   // Staging loads first (NUL pieces per thread), then the first weight units, then the
   // LDS stores: memory counters retire in issue order, so the stores wait for the
@@ -113,7 +145,7 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
   constexpr int D = 3;
   TallUnit rb[D];
 #pragma unroll
-  for (int t = 0; t < D; ++t) tall_load(wr + (wv * 4 + g + 16 * t) * 36, rb[t]);
+  for (int t = 0; t < D; ++t) tall_load(wr + (u_load + 16 * t) * 36, rb[t]);
 #pragma unroll
   for (int i = 0; i < NUL; ++i) {
     const int p = threadIdx.x + 256 * i;
@@ -130,7 +162,15 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < NUL; ++t) {
-    const TallUnit& u = rb[t % D];
+    TallUnit u;
+    if constexpr (STAGED) {
+      stage_put(t & 1, rb[t % D]);
+      if (t + D < NUL) tall_load(wr + (u_load + 16 * (t + D)) * 36, rb[t % D]);
+      __syncthreads();
+      u = stage_get(t & 1);
+    } else {
+      u = rb[t % D];
+    }
     const int un = wv * 4 + g + 16 * t;
     const uint4* a0 = (live && bl == 0) ? tall_xs + 16 * un + hl : zero;
     const uint4* a1 = (live && bl == 1) ? tall_xs + 16 * un + 8 + hl : zero;
@@ -150,7 +190,8 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
     acc[1] = __builtin_fmaf(tall_scale<1>(u.d[4]), dd[1], acc[1]);
     acc[2] = __builtin_fmaf(tall_scale<2>(u.d[8]), dd[2], acc[2]);
     acc[3] = __builtin_fmaf(tall_scale<3>(u.d[8]), dd[3], acc[3]);
-    if (t + D < NUL) tall_load(wr + (wv * 4 + g + 16 * (t + D)) * 36, rb[t % D]);
+    if constexpr (!STAGED)
+      if (t + D < NUL) tall_load(wr + (u_load + 16 * (t + D)) * 36, rb[t % D]);
   }
   // Sum over the four half sums, the four lane groups, then the four wavefronts (in a
   // fixed order); the 1/2 of the half-scale is applied at the store.
@@ -165,13 +206,15 @@ __global__ __launch_bounds__(256) void gemv_tall_kernel(const TallParts parts,
 
 // Whether a batch-1 launch takes the tall kernel. A forced kernel (rfp4_force) turns it
 // off (dot product, tiles, no-tall) or on wherever the shape allows (tall). By default,
-// from timings against the dot-product kernel on one machine: fused launches of several
-// matrices only (gate + up 21.8 against 22.9 us, q + k + v 6.5 against 6.9; on one matrix
-// the dot-product kernel, which keeps its weight units in flight, was 4-8 % faster at
-// 8192-24576 and 49152 rows and within 1 % elsewhere up to 152064), k = 5120 only (at
-// k = 6144 it was 7-10 % slower from 12288 rows), at least two tiles per CU, and the
-// busiest CU at most 7 % above the average tile count (at 17408 rows, 4.25 tiles per
-// CU, it was 2-5 % slower).
+// from timings against the dot-product kernel on one machine (tall / dot, us): fused
+// launches of several matrices (gate + up 21.0 / 22.9, q + k + v 6.5 / 6.8) and single
+// matrices with at least 8 tiles per CU, where the tall kernel stages its weights
+// (32768 rows 19.3 / 20.8, 34816 rows 20.9 / 22.2, 69632 rows 36.8 / 39.4, 152064 rows
+// 75.4 / 82.2; below that the dot-product kernel, which keeps its weight units in flight,
+// was 3-8 % faster: 16384 rows 11.5 / 11.2, 24576 rows 16.1 / 14.9); k = 5120 only (at
+// k = 6144 it was 7-10 % slower from 12288 rows); at least two tiles per CU, and the
+// busiest CU at most 7 % above the average tile count (at 17408 rows, 4.25 tiles per CU,
+// it was 2-5 % slower).
 inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb, int batch,
                            const Force& force) {
   if (layout != kDual || batch != 1 || (nb != 160 && nb != 192)) return false;
@@ -184,8 +227,9 @@ inline bool gemv_tall_fits(const GemvPart* parts, int count, int layout, int nb,
   const int fk = force.gemv_kernel;
   if (fk == RFP4_GEMV_KERNEL_DOT || fk == RFP4_GEMV_KERNEL_TILES || fk == RFP4_GEMV_KERNEL_NO_TALL) return false;
   if (fk == RFP4_GEMV_KERNEL_TALL) return true;
-  if (nb != 160 || count < 2) return false;
+  if (nb != 160) return false;
   const int64_t cus = device_cu_count();
+  if (count < 2 && tiles < 8 * cus) return false;
   const int64_t busiest = (tiles + cus - 1) / cus;
   return tiles >= 2 * cus && busiest * cus * 100 <= tiles * 107;
 }
@@ -206,14 +250,22 @@ inline hipError_t launch_gemv_tall(const GemvPart* parts, int count, int nb, con
     tp.tbeg[i + 1] = tp.tbeg[count];
   }
   const dim3 grid(tp.tbeg[count]), block(256);
-  const size_t shm = (static_cast<size_t>(nb) * 8 + 8) * 16;
+  // The weight stage from 8 tiles per CU (measured against per-lane loads, us: fused
+  // gate + up 2 x 17408 rows, 8.5 tiles per CU, 21.86 -> 20.97; 2 x 34816 rows 39.46 ->
+  // 37.92; 2 x 76032 rows 81.62 -> 76.95; but 2 x 8192 rows, 4 per CU, 10.72 -> 11.26 and
+  // q + k + v, 2 per CU, 6.51 -> 7.25: with few workgroups per CU its barriers are not
+  // hidden).
+  const bool staged = tp.tbeg[count] >= 8 * device_cu_count();
+  const size_t shm = (static_cast<size_t>(nb) * 8 + 8 + (staged ? 2 * 576 : 0)) * 16;
+#define RFP4_TALL_LAUNCH(NU, SG, ST) gemv_tall_kernel<NU, SG, ST><<<grid, block, shm, stream>>>(tp, x)
   if (nb == 160) {
-    if (count == 1) gemv_tall_kernel<5, true><<<grid, block, shm, stream>>>(tp, x);
-    else gemv_tall_kernel<5, false><<<grid, block, shm, stream>>>(tp, x);
+    if (count == 1) { if (staged) RFP4_TALL_LAUNCH(5, true, true); else RFP4_TALL_LAUNCH(5, true, false); }
+    else { if (staged) RFP4_TALL_LAUNCH(5, false, true); else RFP4_TALL_LAUNCH(5, false, false); }
   } else {
-    if (count == 1) gemv_tall_kernel<6, true><<<grid, block, shm, stream>>>(tp, x);
-    else gemv_tall_kernel<6, false><<<grid, block, shm, stream>>>(tp, x);
+    if (count == 1) { if (staged) RFP4_TALL_LAUNCH(6, true, true); else RFP4_TALL_LAUNCH(6, true, false); }
+    else { if (staged) RFP4_TALL_LAUNCH(6, false, true); else RFP4_TALL_LAUNCH(6, false, false); }
   }
+#undef RFP4_TALL_LAUNCH
   return hipGetLastError();
 }
 

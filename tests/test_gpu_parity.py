@@ -411,6 +411,29 @@ def test_gemv_tall_default_fused_gate_up_sampled():
         assert O.normalized_error(y.cpu().numpy()[:, rows], y_ref, den) <= TOL
 
 
+@pytest.mark.parametrize("n,kernel", [(32768, "auto"), (33792, "tall")])
+def test_gemv_tall_staged_sampled(n, kernel, force):
+    """From 8 tiles per CU the tall kernel loads its weights along rows and hands them to
+    the multiplying lanes through a double-buffered LDS stage: a single 32768-row matrix
+    takes it by default, and 33792 rows (tiles spread unevenly over the CUs) when forced.
+    Weights include 2 % stress blocks; seeded sampled rows (both ends of the matrix and
+    of tiles included) against the oracle, and every row against the dot-product kernel."""
+    layout, k = 0, 5120
+    rng = np.random.default_rng(9970 + n)
+    w = synth.weights(rng, layout, n, k, stress_frac=0.02)
+    x = synth.activations(rng, 1, k, "f16")
+    wd, xd = dev(w), x.to(DEV).contiguous()
+    force(gemv_kernel=kernel)
+    y = R.rfp4_gemv(wd, layout, n, k, xd).cpu().numpy()
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 4095, 4096, n - 17, n - 16, n - 1],
+                                     rng.choice(n, 96, replace=False)]))
+    y_ref, den = O.gemv_rows(w, layout, n, k, x64(x), rows)
+    assert O.normalized_error(y[:, rows], y_ref, den) <= TOL
+    force(gemv_kernel="dot")
+    y_dot = R.rfp4_gemv(wd, layout, n, k, xd).cpu().numpy()
+    assert np.all(np.isfinite(y)) and np.allclose(y, y_dot, rtol=2e-3, atol=1e-3 * np.abs(y_dot).max())
+
+
 def test_gemv_zero_scales_give_zero():
     rng = np.random.default_rng(31)
     n, k = 64, 1024
