@@ -38,8 +38,8 @@
 //
 // The four wavefronts' 16 x 16 accumulator tiles are added in LDS in a fixed order and
 // the batch rows are stored. Long rows on few tiles split each tile's chunks between
-// two workgroups (see mfma_splits); the last of them to finish adds both parts in a
-// fixed order.
+// two to four workgroups (see mfma_splits); the last of them to finish adds the parts in
+// a fixed order.
 
 #pragma once
 
@@ -113,7 +113,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   constexpr int G = 4 * W;        // lane groups: units of a row per chunk
   constexpr int PU = 4 * P;       // 16-byte activation pieces per unit
   constexpr int XPT = BIG ? 2 * P : P;  // pieces per thread per chunk: batch <= 8 or <= 4
-  constexpr int D = R == 2 ? 2 : 3;     // chunks in flight (two with two tiles: registers)
+  // Chunks in flight. Two rather than three: 113-116 instead of 140-146 registers at
+  // batches above 4 (one tile per workgroup), so four workgroups fit on a CU instead of
+  // three, which the k-range split below turns into more wavefronts per CU; measured
+  // (same box, us) 5120 x 17408 batch 3/8 19.0/23.5 -> 17.8/22.2 at the same split,
+  // 5120 x 6144 batch 8 12.0 -> 11.2, 17408 x 5120 batch 4 16.7 -> 16.0.
+  constexpr int D = 2;
   // LDS pieces per activation row of a chunk: G units of PU + 1 pieces, plus one piece so
   // that consecutive rows start 16 bytes apart modulo 256. The 16 lanes of a lane group
   // read the same piece of up to 8 different rows in one access; with rows a multiple of
@@ -188,8 +193,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   // of activation row b, stored at LDS unit b XROW + u (PU + 1) + p; consecutive threads
   // read consecutive pieces of a row. The loads are clamped to the last piece (and to
   // the row's last unit), so every thread loads XPT pieces in bounds; pieces of units
-  // past the row end are zeroed, so the zeroed weights there meet zeros (0 * inf would
-  // be NaN).
+  // past the row end are stored as zeros, so the weights there meet zeros (0 * inf would
+  // be NaN). The zeroing happens at the LDS store, which waits for the load anyway: a
+  // select applied to the loaded registers is free to be placed anywhere after the load,
+  // and placed early it makes the wavefront wait for loads of chunks still meant to be in
+  // flight.
   const int pieces = batch * G * PU;
   struct XChunk {
     uint4 v[XPT];
@@ -203,23 +211,23 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
       const int bu = i / PU;
       const int b = bu / G;
       const int unit = G * (t_off + t) + (bu % G);
-      const uint4 v = *reinterpret_cast<const uint4*>(x + b * ldx + 32 * P * min(unit, nu - 1) + 8 * p);
-      c.v[j] = unit < nu ? v : uint4{0u, 0u, 0u, 0u};
+      c.v[j] = *reinterpret_cast<const uint4*>(x + b * ldx + 32 * P * min(unit, nu - 1) + 8 * p);
     }
     return c;
   };
-  auto x_store = [&](XChunk c) {
+  auto x_store = [&](const XChunk& c, int t) {
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = static_cast<int>(threadIdx.x) + j * THREADS;
       if (i < pieces) {
         const int bu = i / PU;
-        xs[(bu / G) * XROW + (bu % G) * (PU + 1) + i % PU] = c.v[j];
+        const bool live = G * (t_off + t) + (bu % G) < nu;
+        xs[(bu / G) * XROW + (bu % G) * (PU + 1) + i % PU] = live ? c.v[j] : uint4{0u, 0u, 0u, 0u};
       }
     }
   };
 
-  // Three chunks in flight: the activations and weights of chunk t are loaded together,
+  // D chunks in flight: the activations and weights of chunk t are loaded together,
   // so the LDS stores of chunk t wait for exactly those loads and leave the later chunks
   // in flight.
   XChunk xr[D];
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   };
 
   // Per chunk: wait until every wavefront is done with the previous chunk, store this
-  // one, wait until it is complete, multiply; then issue chunk t + 3. Rounds of three
+  // one, wait until it is complete, multiply; then issue chunk t + D. Rounds of D
   // chunks keep the register rings indexed by constants. Every round but the last
   // loads unconditionally (clamped to the last chunk), since a path that skipped loads
   // would make the compiler's load waits count the shortest path; the last round loads
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (t + d > 0) __syncthreads();
-      x_store(xr[d]);
+      x_store(xr[d], t + d);
       w_store(d);
       __syncthreads();
       consume(d);
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   for (int d = 0; d < D; ++d) {
     if (t + d < T) {
       if (t + d > 0) __syncthreads();
-      x_store(xr[d]);
+      x_store(xr[d], t + d);
       w_store(d);
       __syncthreads();
       consume(d);
@@ -431,27 +439,49 @@ struct MfmaPlan {
   size_t shm;
 };
 
-// Split chunks: launches of long rows and few tiles give each tile's chunks to two
-// workgroups, so that every CU gets work. Measured (same box, us): 5120 x 17408 (17
-// chunks per row, 320 tiles) batch 2/4/8 22.3/23.8/34.1 unsplit, 20.2/21.9/28.4 in two
-// parts, 21.2/23.4/32.3 in four; rows of 5-6 chunks (6144 x 5120, 5120 x 6144, 1024 x
-// 5120) are slower split, since combining the parts adds round trips to memory at the
-// end of a short launch. The partial sums and arrival counters live in a
-// per-(device, stream) workspace of fixed size: the counters first (a region for up to
-// kMaxSplitTiles tiles, zero at allocation and reset by the last arrival of each
-// tile), then the sums of up to kMaxSplits parts. A forced split (rfp4_force) is
-// reduced to at least one chunk per part.
+// Split chunks: launches of long rows and few tiles give each tile's chunks to several
+// workgroups, so that every CU gets more wavefronts. Measured over 1024-12288 rows of
+// 17408 columns and rows of 6144-13824 columns (graph-replayed launches, batches 3-8), a
+// launch takes about a fixed time plus a per-chunk cost times the chunks that the
+// busiest CU's workgroups hold together, ceil(tiles s / CUs) ceil(chunks / s), with a
+// ~15 % higher per-chunk cost where every CU holds at most one workgroup (one
+// workgroup's wavefronts leave the loads less overlapped). The launcher takes the split
+// s (1 to kMaxSplits) of the lowest such cost, the smaller s on a tie, among those whose
+// workgroups all fit on the CUs at once (`slots`: resident workgroups per CU, from the
+// occupancy of the kernel instance, times the CUs) and whose parts keep at least
+// kMinSplitChunks chunks each (shorter parts lose what they gain to the combining
+// step). Measured (same box, us, parts 1/2/3/4, * = chosen): 5120 x 17408 batch 8
+// 23.6/22.4/21.3*/22.1, 4096 x 17408 batch 8 18.1/17.1*/18.1/18.5, 8192 x 17408 batch 8
+// 25.0*/27.9/29.0/30.0, 1024 x 17408 batch 8 17.7/13.3/11.4*/11.2 (four parts leave four
+// chunks), 4096 x 8192 batch 8 10.3*/11.2/11.9/12.0, 5120 x 6144 batch 8 11.1*/12.2/11.5/13.5.
+// The partial sums and arrival counters live in a per-(device, stream) workspace of fixed
+// size: the counters first (a region for up to kMaxSplitTiles tiles, zero at allocation
+// and reset by the last arrival of each tile), then the sums of up to kMaxSplits parts.
+// A forced split (rfp4_force, 1-4 parts) is reduced to at least one chunk per part.
 constexpr int kMaxSplitTiles = 1024;
 constexpr int kMaxSplits = 4;
+constexpr int kMinSplitChunks = 5;
 constexpr size_t kSplitCounterBytes = kMaxSplitTiles * sizeof(int);
 constexpr size_t kSplitWorkspaceBytes =
     kSplitCounterBytes + static_cast<size_t>(kMaxSplits) * kMaxSplitTiles * 128 * sizeof(float);
-inline int mfma_splits(int tiles, int nu, const Force& force) {
+inline int mfma_splits(int tiles, int nu, int64_t slots, const Force& force) {
   const int t_all = (nu + 4 * kMfmaWaves - 1) / (4 * kMfmaWaves);
-  int s = (tiles < 4 * device_cu_count() && t_all >= 12) ? 2 : 1;
+  const int64_t cus = device_cu_count();
+  int s = 1;
+  int64_t best = 0;
+  for (int c = 1; c <= kMaxSplits; ++c) {
+    const int64_t wgs = static_cast<int64_t>(tiles) * c;
+    if (c > 1 && (wgs > slots || t_all / c < kMinSplitChunks)) continue;
+    // 20 x the cost above: the lone-workgroup factor 1.15 as 23 / 20.
+    const int64_t cost = (wgs + cus - 1) / cus * ((t_all + c - 1) / c) * (wgs <= cus ? 23 : 20);
+    if (c == 1 || cost < best) {
+      best = cost;
+      s = c;
+    }
+  }
   if (force.gemv_splits != 0) s = force.gemv_splits;
   if (tiles > kMaxSplitTiles) s = 1;
-  while (s > 1 && t_all < s) s /= 2;
+  if (s > t_all) s = t_all;
   return s;
 }
 
@@ -479,8 +509,23 @@ inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch, c
   pl.tiles = 0;
   for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 16 * pl.r - 1) / (16 * pl.r));
   pl.shm = mfma_lds(pl.p, batch, pl.r);
-  pl.splits = pl.r == 1 ? mfma_splits(pl.tiles, pl.nu, force) : 1;
+  pl.splits = 1;  // set by the launcher (it depends on the kernel instance's occupancy)
   return pl;
+}
+
+// Workgroups of a one-tile kernel instance that fit on a CU at once (its registers and
+// the LDS of its largest batch), from the runtime's occupancy calculator; computed once
+// per instance.
+template <int LAYOUT, int XT, int P, bool BIG, int NP>
+int mfma_resident() {
+  static const int n = [] {
+    int b = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &b, reinterpret_cast<const void*>(&gemv_mfma_kernel<LAYOUT, XT, P, BIG, 1, NP>), 64 * kMfmaWaves,
+        mfma_lds(P, BIG ? 8 : 4, 1));
+    return e == hipSuccess && b > 0 ? b : 1;
+  }();
+  return n;
 }
 
 template <int LAYOUT, int XT, int P, bool BIG, int NP>
@@ -500,6 +545,13 @@ template <int LAYOUT, int XT, int NP>
 hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t* x, int batch,
                        int64_t ldx, const Force& force, hipStream_t stream) {
   MfmaPlan pl = mfma_plan(parts, count, nb, batch, force);
+  if (pl.r == 1) {
+    const int resident = pl.p == 2 ? (pl.big ? mfma_resident<LAYOUT, XT, 2, true, NP>()
+                                             : mfma_resident<LAYOUT, XT, 2, false, NP>())
+                                   : (pl.big ? mfma_resident<LAYOUT, XT, 1, true, NP>()
+                                             : mfma_resident<LAYOUT, XT, 1, false, NP>());
+    pl.splits = mfma_splits(pl.tiles, pl.nu, static_cast<int64_t>(resident) * device_cu_count(), force);
+  }
   float* partial = nullptr;
   int* arrivals = nullptr;
   if (pl.splits > 1) {

@@ -54,8 +54,7 @@ rfp4_status check_force(const rfp4_force* force, rfp4::Force* out) {
     if (f.gemv_unit_blocks != 1 && f.gemv_unit_blocks != 2) return RFP4_ERR_UNSUPPORTED;
     if (cl < 1 || cl > 64 || (cl & (cl - 1)) != 0) return RFP4_ERR_UNSUPPORTED;
   }
-  if (f.gemv_splits != 0 && f.gemv_splits != 1 && f.gemv_splits != 2 && f.gemv_splits != 4)
-    return RFP4_ERR_UNSUPPORTED;
+  if (f.gemv_splits < 0 || f.gemv_splits > 4) return RFP4_ERR_UNSUPPORTED;
   if (f.gemm_plan < RFP4_GEMM_PLAN_AUTO || f.gemm_plan > RFP4_GEMM_PLAN_NOSPLIT) return RFP4_ERR_UNSUPPORTED;
   *out = f;
   return RFP4_OK;

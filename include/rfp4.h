@@ -223,7 +223,7 @@ typedef struct rfp4_force {
                                   mapping (a pair mapping on an odd k / 32 is ignored) */
   int32_t gemv_lanes_per_row;  /* dot-product kernel: lanes per weight row, a power of two
                                   from 1 to 64 (0 with gemv_unit_blocks = 0) */
-  int32_t gemv_splits;         /* tile kernel: parts of each tile's k range, 1, 2 or 4
+  int32_t gemv_splits;         /* tile kernel: parts of each tile's k range, 1 to 4
                                   (fewer where a row has fewer chunks); 0 = default */
   int32_t gemm_plan;           /* rfp4_gemm_plan */
 } rfp4_force;

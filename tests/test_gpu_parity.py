@@ -1000,12 +1000,13 @@ SPLIT_CASES = [  # layout, n, k, batch, dtype, forced split (reduced to one chun
     (1, 5120, 17408, 8, "bf16", 2), (1, 5120, 17408, 2, "bf16", 4), (0, 1024, 5120, 3, "f16", 4),
     (0, 33, 1408, 4, "f16", 2), (0, 1, 256, 5, "f16", 4), (1, 45, 1056, 6, "bf16", 4),
     (0, 300, 4000, 8, "bf16", 4), (0, 999, 2304, 7, "f16", 2), (1, 5120, 6144, 4, "bf16", 1),
+    (1, 5120, 17408, 8, "bf16", 3), (0, 300, 4000, 6, "f16", 3), (1, 45, 1056, 3, "bf16", 3),
 ]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "L{}n{}k{}b{}{}-s{}".format(*c))
 def test_gemv_mfma_split(case, force):
-    """Each tile's chunks shared by 1, 2 or 4 workgroups whose partial sums meet in the
+    """Each tile's chunks shared by 1 to 4 workgroups whose partial sums meet in the
     stream's workspace; padded output rows stay untouched."""
     layout, n, k, batch, dt, split = case
     force(gemv_kernel="tiles", gemv_splits=int(split))
@@ -1019,7 +1020,7 @@ def test_gemv_mfma_split_launch_sequence(force):
     """Launches with different splits and tile counts back to back on one stream (the
     arrival counters must be back at zero after each), then the first one again."""
     rng = np.random.default_rng(9450)
-    shapes = [(0, 700, 2048, 4, 4), (1, 130, 6144, 8, 2), (0, 700, 2048, 4, 2), (0, 64, 5120, 2, 4),
+    shapes = [(0, 700, 2048, 4, 4), (1, 130, 6144, 8, 2), (0, 700, 2048, 4, 3), (0, 64, 5120, 2, 4),
               (0, 700, 2048, 4, 4)]
     data = {}
     for layout, n, k, batch, _ in shapes:
