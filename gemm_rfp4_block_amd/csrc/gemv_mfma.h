@@ -502,10 +502,14 @@ inline MfmaPlan mfma_plan(const GemvPart* parts, int count, int nb, int batch, c
   for (int i = 0; i < count; ++i) tiles16 += static_cast<int>((parts[i].n + 15) / 16);
   pl.big = batch > 4;
   // Two tiles per workgroup (sharing each staged activation chunk) for batches above 4
-  // on launches of many tiles: 152064 x 5120 batch 5/8 145.8/156.1 -> 120.0/127.9 us,
-  // 17408 x 5120 batch 8 24.2 -> 23.6 us; at batches <= 4 it was slower on 17408 x 5120
-  // (16.7 -> 19.4 us at batch 2).
-  pl.r = (pl.big && tiles16 >= 4 * device_cu_count()) ? 2 : 1;
+  // on launches of at least six 16-row tiles per CU. Measured against one tile per
+  // workgroup (same box, us, batch 5 / batch 8): 152064 x 5120 104.2 / 111.9 against
+  // 115.5 / 127.6, 32768 x 5120 26.3 / 27.8 against 27.8 / 30.7, 24576 x 5120 20.5 / 21.7
+  // against 21.5 / 24.1, fused gate + up (2 x 17408 rows) 29.6 / 31.6 against 29.9 / 33.0;
+  // below six tiles per CU one tile per workgroup (four workgroups per CU) is ahead:
+  // 20480 x 5120 19.8 / 21.0 against 18.9 / 21.3, 17408 x 5120 19.5 / 20.6 against
+  // 17.4 / 19.6. At batches <= 4 two tiles were slower (17408 x 5120 batch 2 16.7 -> 19.4).
+  pl.r = (pl.big && tiles16 >= 6 * device_cu_count()) ? 2 : 1;
   pl.tiles = 0;
   for (int i = 0; i < count; ++i) pl.tiles += static_cast<int>((parts[i].n + 16 * pl.r - 1) / (16 * pl.r));
   pl.shm = mfma_lds(pl.p, batch, pl.r);
@@ -584,22 +588,24 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
 // Matrix-core path for the launches where it is faster. Measured (graph-replayed
 // launches over rotating weight copies, one machine, dot-product / matrix cores, us):
 // the dot-product kernel wins at batch 1 (its decode needs no table, no staging and no
-// cross-wave reduction) and at batch 2 on one matrix (17408 x 5120 16.31 / 16.78,
-// 5120 x 17408 17.51 / 19.29, 5120 x 6144 9.46 / 9.85, 1024 x 5120 4.75 / 6.60,
-// 152064 x 5120 92.3 / 100.7, 49152 x 5120 33.5 / 35.4; the matrix cores were ahead by at
-// most 3 % at 3072, 4096 and 34816 rows) and on fused launches below 32768 rows (q + k + v
-// 8.83 / 8.96, k + v 5.92 / 6.31), not on fused gate + up (27.27 / 26.84). From batch 3
-// the matrix cores win (their decode does not grow with the batch), except on one
-// matrix of at most 1024 short rows up to batch 6 (1024 x 5120 batch 3/4/6 5.63 / 6.74,
-// 6.19 / 6.80, 7.25 / 7.49; at batch 8 8.75 / 7.66, and from 2048 rows the tiles lead).
-// A forced kernel (rfp4_force) replaces the choice.
+// cross-wave reduction). At batch 2 the matrix cores win from 4096 to 65536 rows (all
+// matrices of the launch together): 4096 x 5120 7.52 / 6.68, 8192 x 5120 9.00 / 8.64,
+// 17408 x 5120 15.56 / 14.73, 4096 x 17408 14.52 / 14.11, 5120 x 17408 17.48 / 16.70,
+// 5120 x 6144 9.45 / 8.99, fused q + k + v (7168 rows) 11.11 / 8.62, even at 12288 (11.21 /
+// 11.29), 49152 (33.05 / 32.76) and 69632 rows (45.02 / 44.87); the dot-product kernel
+// below (1024 x 5120 4.77 / 6.06, 2048 x 5120 5.92 / 6.25, 2048 x 17408 10.00 / 11.00,
+// 3072 x 17408 12.42 / 13.74; 3072 x 5120 7.21 / 6.51 is the exception) and above
+// (152064 x 5120 93.6 / 95.9). From batch 3 the matrix cores win (their decode does not
+// grow with the batch), except on one matrix of at most 1024 short rows up to batch 6
+// (1024 x 5120 batch 3/4/6 5.68 / 6.26, 6.25 / 6.46, 7.26 / 7.15; at batch 8 8.75 / 7.66,
+// and from 2048 rows the tiles lead). A forced kernel (rfp4_force) replaces the choice.
 inline bool use_mfma(const GemvPart* parts, int count, int nb, int batch, const Force& force) {
   if (force.gemv_kernel == RFP4_GEMV_KERNEL_DOT) return false;
   if (force.gemv_kernel == RFP4_GEMV_KERNEL_TILES) return true;
   if (batch < 2) return false;
   int64_t rows = 0;
   for (int i = 0; i < count; ++i) rows += parts[i].n;
-  if (batch == 2) return count > 1 && rows >= 32768;
+  if (batch == 2) return rows >= 4096 && rows <= 65536;
   if (batch <= 6 && count == 1 && rows <= 1024 && nb <= 192) return false;
   return true;
 }
