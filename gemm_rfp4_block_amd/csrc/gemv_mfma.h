@@ -215,14 +215,22 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     }
     return c;
   };
+  // Only a chunk that reaches past the row end holds dead pieces (a uniform test), so
+  // the others store the loaded registers as they are; the piece count is a multiple of
+  // the block size for the first pieces / THREADS stores of every thread (uniform too).
   auto x_store = [&](const XChunk& c, int t) {
+    const bool ragged = G * (t_off + t + 1) > nu;
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = static_cast<int>(threadIdx.x) + j * THREADS;
-      if (i < pieces) {
+      if ((j + 1) * THREADS <= pieces || i < pieces) {
         const int bu = i / PU;
-        const bool live = G * (t_off + t) + (bu % G) < nu;
-        xs[(bu / G) * XROW + (bu % G) * (PU + 1) + i % PU] = live ? c.v[j] : uint4{0u, 0u, 0u, 0u};
+        uint4 v = c.v[j];
+        if (ragged) {
+          const uint32_t m = G * (t_off + t) + (bu % G) < nu ? ~0u : 0u;
+          v = uint4{v.x & m, v.y & m, v.z & m, v.w & m};
+        }
+        xs[(bu / G) * XROW + (bu % G) * (PU + 1) + i % PU] = v;
       }
     }
   };
