@@ -17,7 +17,8 @@ launches replayed back to back (event time of a replay / 100), so that the GPU n
 waits for the host between these short kernels; the longer kernels (GEMM, dequant,
 encoder) by HIP events around every launch on the stream they run on. A plain
 streaming read of the same weight copies (librfp4_bench.so) gives the HBM read rate a
-kernel of this size reaches. The CPU baseline times the fp64 oracle on the host on every
+kernel of this size reaches, and a dense bf16 MFMA loop of the same library the matrix-core
+rate the chip sustains (the GEMM's practical ceiling). The CPU baseline times the fp64 oracle on the host on every
 workload (tiny, up-projection, down-projection at each batch, the full prefill GEMM).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-sweep] [--no-gemm]
@@ -228,6 +229,33 @@ def read_ceiling(torch, copies, w_bytes, dev):
             "single_800MiB": {"us": round(usb, 2), "GB/s": round(800 * 2**20 / (usb * 1e-6) / 1e9, 1)},
             "kernel": f"rfp4bench_read (16-byte loads, {READ_UNROLL} per lane in flight, "
                       f"{READ_WGS_PER_CU} 256-thread workgroups per CU)"}
+
+
+def mfma_ceiling(torch, dev):
+    """Sustained dense bf16 matrix-core rate on this part (librfp4_bench.so's MFMA loop:
+    v_mfma_f32_32x32x16_bf16 into independent accumulators, operands changing from one
+    instruction to the next, no memory traffic), with one issuing wavefront per SIMD (what
+    each phase of the GEMM's ping-pong schedule has) and with four. The published 2.5
+    PFLOP/s stays the roofline peak; this is the rate the chip holds in practice."""
+    import ctypes
+
+    B = ctypes.CDLL(os.path.join(ROOT, "gemm_rfp4_block_amd", "_lib", "librfp4_bench.so"))
+    B.rfp4bench_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {}
+    for key, wgs, threads, iters in (("one_wave_per_simd", 1, 256, 2048), ("four_waves_per_simd", 2, 512, 512)):
+        def fn(i, wgs=wgs, threads=threads, iters=iters):
+            st = B.rfp4bench_mfma(wgs, threads, iters, ctypes.c_void_p(sink.data_ptr()),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"rfp4bench_mfma failed: {st}")
+        warm_up(torch, fn, 0.3)
+        d = stats_us(timed_launches(torch, fn, 10))
+        flops = cus * wgs * (threads // 64) * iters * 8 * 32 * 32 * 16 * 2
+        out[key] = {"TFLOP/s": round(flops / (d["mean_us"] * 1e-6) / 1e12, 1), "us": round(d["mean_us"], 1)}
+    out["kernel"] = "rfp4bench_mfma (8 independent v_mfma_f32_32x32x16_bf16 chains per wavefront, hashed operands)"
+    return out
 
 
 GUARD_KEYS = [  # (path in the JSON line, True if lower is better)
@@ -668,6 +696,12 @@ def main():
                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": gtraffic},
                 **{kk: round(v, 2) for kk, v in d.items()}}
         log(f"gemm: mean {d['mean_us']:.1f} us -> {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
+        mc = mfma_ceiling(torch, dev)
+        gemm["mfma_ceiling"] = mc
+        gemm["roofline"]["frac_of_sustained_mfma"] = round(tf / mc["four_waves_per_simd"]["TFLOP/s"], 4)
+        log(f"sustained bf16 MFMA rate: {mc['four_waves_per_simd']['TFLOP/s']:.0f} TFLOP/s (four waves per SIMD), "
+            f"{mc['one_wave_per_simd']['TFLOP/s']:.0f} (one); the GEMM runs at "
+            f"{gemm['roofline']['frac_of_sustained_mfma']:.1%} of the former")
         # the dequantize-then-multiply baseline (bf16 expansion + rocBLAS dense GEMM)
         wbuf = torch.empty((gn, gk), dtype=torch.bfloat16, device=dev)
         call_fb = lambda i: R.rfp4_gemm_dequant(gcopies[i % ngc], gcfg["layout"], gn, gk, a, wbuf, c)

@@ -50,6 +50,33 @@ def test_library_exports_every_declared_symbol(L):
     assert exported == set(declared_functions())
 
 
+BENCH_HEADER = os.path.join(ROOT, "include", "rfp4_bench.h")
+BENCH_LIB = os.path.join(ROOT, "gemm_rfp4_block_amd", "_lib", "librfp4_bench.so")
+
+
+def test_bench_library_exports_its_header_and_checks_arguments(L):
+    """librfp4_bench.so (the read and matrix-core ceilings of the benchmark) exports
+    exactly what include/rfp4_bench.h declares and rejects bad arguments before any HIP
+    call (-1), so this runs without a GPU."""
+    declared = sorted(set(re.findall(r"\b(rfp4bench_\w+)\s*\(", open(BENCH_HEADER).read())))
+    assert declared == ["rfp4bench_mfma", "rfp4bench_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", BENCH_LIB], capture_output=True, text=True)
+    assert set(re.findall(r" T (rfp4bench_\w+)", out.stdout)) == set(declared)
+    B = ctypes.CDLL(BENCH_LIB)
+    B.rfp4bench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    B.rfp4bench_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = ctypes.c_void_p(0x10000)
+    for p, nbytes, unroll, wgs, snk in ((None, 64, 1, 8, sink), (0x10000, 0, 1, 8, sink), (0x10000, 24, 1, 8, sink),
+                                        (0x10008, 64, 1, 8, sink), (0x10000, 64, 3, 8, sink),
+                                        (0x10000, 64, 1, 0, sink), (0x10000, 64, 1, 33, sink),
+                                        (0x10000, 64, 1, 8, None)):
+        assert B.rfp4bench_read(p, nbytes, unroll, wgs, snk, None) == -1
+    for wgs, threads, iters, snk in ((0, 256, 1, sink), (9, 256, 1, sink), (1, 192, 1, sink), (1, 1024, 1, sink),
+                                     (1, 256, 0, sink), (1, 256, 1, None)):
+        assert B.rfp4bench_mfma(wgs, threads, iters, snk, None) == -1
+
+
 def test_block_and_row_bytes(L):
     assert R.rfp4_block_bytes(R.RFP4_DUAL) == O.block_bytes(O.DUAL) == 18
     assert R.rfp4_block_bytes(R.RFP4_FAST) == O.block_bytes(O.FAST) == 17
