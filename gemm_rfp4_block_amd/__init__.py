@@ -46,16 +46,17 @@ class Force(ctypes.Structure):
 
     _fields_ = [("gemv_kernel", ctypes.c_int32), ("gemv_unit_blocks", ctypes.c_int32),
                 ("gemv_lanes_per_row", ctypes.c_int32), ("gemv_splits", ctypes.c_int32),
-                ("gemm_plan", ctypes.c_int32)]
+                ("gemm_plan", ctypes.c_int32), ("gemv_split_combine", ctypes.c_int32)]
 
 
 def make_force(gemv_kernel: str = "auto", gemv_plan: tuple | None = None, gemv_splits: int = 0,
-               gemm_plan: str = "auto") -> Force:
+               gemm_plan: str = "auto", gemv_split_combine: int = 0) -> Force:
     """An rfp4_force from names: gemv_kernel in GEMV_KERNEL, gemv_plan = (blocks per lane
     unit, lanes per row) of the dot-product kernel, gemv_splits of the tile kernel,
-    gemm_plan in GEMM_PLAN."""
+    gemm_plan in GEMM_PLAN, gemv_split_combine (1: the split tiles' parts combine without
+    the last part's polling)."""
     p, cl = gemv_plan if gemv_plan is not None else (0, 0)
-    return Force(GEMV_KERNEL[gemv_kernel], p, cl, gemv_splits, GEMM_PLAN[gemm_plan])
+    return Force(GEMV_KERNEL[gemv_kernel], p, cl, gemv_splits, GEMM_PLAN[gemm_plan], gemv_split_combine)
 
 
 class Rfp4Error(RuntimeError):

@@ -101,12 +101,17 @@ __device__ __forceinline__ void unit_scale_bytes(const UnitRaw<P>& u, uint32_t& 
 
 constexpr int kMfmaWaves = 4;
 
+// Polls of the arrival counter by a combining part before it falls back to storing and
+// counting its own sums (each poll is a round trip to the coherence point plus a short
+// sleep: together a few microseconds, longer than the parts normally lag each other).
+constexpr int kCombinerPolls = 24;
+
 template <int LAYOUT, int XT, int P, bool BIG, int R, int NP>
 __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvParts<NP> parts, int nu,
                                                            const uint16_t* __restrict__ x,
                                                            int64_t ldx, int batch, int splits,
                                                            float* __restrict__ partial,
-                                                           int* __restrict__ arrivals) {
+                                                           int* __restrict__ arrivals, int polls) {
   constexpr int W = kMfmaWaves;
   constexpr int UB = P * block_bytes(LAYOUT);
   constexpr int THREADS = 64 * W;
@@ -386,33 +391,58 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   }
   const int row = r0 + col;
   if (R == 1 && splits > 1) {
-    // Leave this part's sums (tile-major, weight row, batch row), then let the last part
-    // to arrive add all parts in part order, so the result does not depend on the
+    // Parts leave their sums (tile-major, weight row, batch row) and count themselves;
+    // one part adds all parts in part order, so the result does not depend on the
     // arrival order.
     // Ordering. Every access to the sums and counters is an agent-scope atomic, which
     // gfx950 code carries out at the device's coherence point: the stores write
     // through (sc1), the loads bypass the non-coherent caches (sc1), the counter is an
     // atomic read-modify-write. s_waitcnt(0) holds the counter update back until every
     // store of this wavefront has completed, so a part that counts itself has its sums
-    // in coherent memory; the last part's loads are issued only after its counter
-    // update has returned (its value decides whether they run), so they read every
-    // part's sums. A release on the counter and an acquire after it would compile to the
+    // in coherent memory; the combining part's loads are issued only after its counter
+    // update, or its poll of the counter, has returned the value that lets them run, so
+    // they read every counted part's sums. A release on the counter and an acquire after it would compile to the
     // same instructions plus a write-back and an invalidation of the whole L2
     // (buffer_wbl2 sc1, buffer_inv sc1), which only matter for data written or read
     // without sc1 (there is none here) and measured 3-5x slower on these launches.
-    float* const mine = partial + (static_cast<int64_t>(part) * tiles + tile) * 128;
-    if (lane < 32) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(&mine[col * 8 + 4 * (lane >> 4) + i], acc[0][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Combining. The last part (dispatched last, so normally the last to finish) is the
+    // combiner: it polls the arrival counter (a bounded number of times) until the other
+    // splits - 1 parts have counted themselves, then reads their sums and adds its own
+    // from registers, without storing them or counting itself; that saves the round trips
+    // of its own stores and counter update at the end of the launch. A combiner that
+    // stops polling before the others have arrived falls back to the general protocol:
+    // it stores and counts itself like the others, and whichever part counts last adds
+    // all parts from memory. Either way the parts are added in part order, so the result
+    // does not depend on which path ran, and the poll is bounded, so no wavefront waits
+    // for another indefinitely. The counter is reset by the part that combined (every
+    // other part has counted itself by then).
+    const bool combiner = part == splits - 1;
+    int seen = 0;
+    if (combiner && lane == 0) {
+      for (int it = 0; it < polls; ++it) {
+        seen = __hip_atomic_load(&arrivals[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seen == splits - 1) break;
+        __builtin_amdgcn_s_sleep(4);
+      }
     }
+    const bool fast = combiner && __shfl(seen, 0, 64) == splits - 1;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    int prior = 0;
-    if (lane == 0) prior = __hip_atomic_fetch_add(&arrivals[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__shfl(prior, 0, 64) != splits - 1) return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (!fast) {
+      float* const mine = partial + (static_cast<int64_t>(part) * tiles + tile) * 128;
+      if (lane < 32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(&mine[col * 8 + 4 * (lane >> 4) + i], acc[0][i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      int prior = 0;
+      if (lane == 0) prior = __hip_atomic_fetch_add(&arrivals[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__shfl(prior, 0, 64) != splits - 1) return;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
     if (lane < 32 && row < n_part) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -420,8 +450,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
         if (b < batch) {
           float sum = 0.f;
           for (int q = 0; q < splits; ++q)
-            sum += __hip_atomic_load(&partial[(static_cast<int64_t>(q) * tiles + tile) * 128 + col * 8 + b],
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sum += (fast && q == splits - 1)
+                       ? acc[0][i]
+                       : __hip_atomic_load(&partial[(static_cast<int64_t>(q) * tiles + tile) * 128 + col * 8 + b],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           y[b * ldy + row] = sum;
         }
       }
@@ -542,14 +574,14 @@ int mfma_resident() {
 
 template <int LAYOUT, int XT, int P, bool BIG, int NP>
 hipError_t launch_mfma_p(const MfmaPlan& pl, const GemvParts<NP>& gp, const uint16_t* x, int64_t ldx,
-                         int batch, float* partial, int* arrivals, hipStream_t stream) {
+                         int batch, float* partial, int* arrivals, int polls, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(pl.tiles) * pl.splits), block(64 * kMfmaWaves);
   if (BIG && pl.r == 2)
     gemv_mfma_kernel<LAYOUT, XT, P, BIG, BIG ? 2 : 1, NP><<<grid, block, pl.shm, stream>>>(
-        gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals);
+        gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals, polls);
   else
     gemv_mfma_kernel<LAYOUT, XT, P, BIG, 1, NP><<<grid, block, pl.shm, stream>>>(
-        gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals);
+        gp, pl.nu, x, ldx, batch, pl.splits, partial, arrivals, polls);
   return hipGetLastError();
 }
 
@@ -576,6 +608,7 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
       partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCounterBytes);
     }
   }
+  const int polls = force.gemv_split_combine == 1 ? 0 : kCombinerPolls;
   GemvParts<NP> gp;
   gp.count = count;
   gp.gbeg[0] = 0;
@@ -587,10 +620,10 @@ hipError_t launch_mfma(const GemvPart* parts, int count, int nb, const uint16_t*
     gp.gbeg[i + 1] = gp.gbeg[i] + static_cast<int>((parts[i].n + 16 * pl.r - 1) / (16 * pl.r));
   }
   if (pl.p == 2)
-    return pl.big ? launch_mfma_p<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream)
-                  : launch_mfma_p<LAYOUT, XT, 2, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream);
-  return pl.big ? launch_mfma_p<LAYOUT, XT, 1, true, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream)
-                : launch_mfma_p<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, stream);
+    return pl.big ? launch_mfma_p<LAYOUT, XT, 2, true, NP>(pl, gp, x, ldx, batch, partial, arrivals, polls, stream)
+                  : launch_mfma_p<LAYOUT, XT, 2, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, polls, stream);
+  return pl.big ? launch_mfma_p<LAYOUT, XT, 1, true, NP>(pl, gp, x, ldx, batch, partial, arrivals, polls, stream)
+                : launch_mfma_p<LAYOUT, XT, 1, false, NP>(pl, gp, x, ldx, batch, partial, arrivals, polls, stream);
 }
 
 // Matrix-core path for the launches where it is faster. Measured (graph-replayed

@@ -55,6 +55,7 @@ rfp4_status check_force(const rfp4_force* force, rfp4::Force* out) {
     if (cl < 1 || cl > 64 || (cl & (cl - 1)) != 0) return RFP4_ERR_UNSUPPORTED;
   }
   if (f.gemv_splits < 0 || f.gemv_splits > 4) return RFP4_ERR_UNSUPPORTED;
+  if (f.gemv_split_combine != 0 && f.gemv_split_combine != 1) return RFP4_ERR_UNSUPPORTED;
   if (f.gemm_plan < RFP4_GEMM_PLAN_AUTO || f.gemm_plan > RFP4_GEMM_PLAN_NOSPLIT) return RFP4_ERR_UNSUPPORTED;
   *out = f;
   return RFP4_OK;

@@ -226,6 +226,13 @@ typedef struct rfp4_force {
   int32_t gemv_splits;         /* tile kernel: parts of each tile's k range, 1 to 4
                                   (fewer where a row has fewer chunks); 0 = default */
   int32_t gemm_plan;           /* rfp4_gemm_plan */
+  int32_t gemv_split_combine;  /* tile kernel with a split k range: 0 = the default (the
+                                  last part polls, a bounded number of times, until the
+                                  others have counted themselves, then adds all parts);
+                                  1 = no polling: every part stores and counts itself
+                                  and the part that counts last adds all parts (the
+                                  default's fallback). Both add the parts in part order,
+                                  so outputs are bitwise equal. */
 } rfp4_force;
 
 /* rfp4_gemv_multi with `force` (may be NULL); rfp4_gemv is count = 1. */

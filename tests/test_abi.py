@@ -224,6 +224,7 @@ BAD_FORCES = [  # each field outside the values include/rfp4.h lists
     dict(gemv_unit_blocks=1, gemv_lanes_per_row=12), dict(gemv_unit_blocks=2, gemv_lanes_per_row=128),
     dict(gemv_unit_blocks=1, gemv_lanes_per_row=0), dict(gemv_unit_blocks=0, gemv_lanes_per_row=8),
     dict(gemv_splits=5), dict(gemv_splits=-1), dict(gemm_plan=9), dict(gemm_plan=-2),
+    dict(gemv_split_combine=2), dict(gemv_split_combine=-1),
 ]
 
 

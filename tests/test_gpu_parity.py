@@ -1007,18 +1007,24 @@ SPLIT_CASES = [  # layout, n, k, batch, dtype, forced split (reduced to one chun
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "L{}n{}k{}b{}{}-s{}".format(*c))
 def test_gemv_mfma_split(case, force):
     """Each tile's chunks shared by 1 to 4 workgroups whose partial sums meet in the
-    stream's workspace; padded output rows stay untouched."""
+    stream's workspace; padded output rows stay untouched. Both ways of combining the
+    parts (the last part polling for the others, and every part counting itself with the
+    last to count adding) match the oracle and each other bitwise."""
     layout, n, k, batch, dt, split = case
-    force(gemv_kernel="tiles", gemv_splits=int(split))
     rng = np.random.default_rng(9400 + n + k + batch)
     w = synth.weights(rng, layout, n, k, stress_frac=0.02)
     x = synth.activations(rng, batch, k, dt)
-    check_gemv(w, layout, n, k, x, ldy=n + 5)
+    ys = []
+    for combine in (0, 1):
+        force(gemv_kernel="tiles", gemv_splits=int(split), gemv_split_combine=combine)
+        ys.append(check_gemv(w, layout, n, k, x, ldy=n + 5)[0])
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
 
 
 def test_gemv_mfma_split_launch_sequence(force):
-    """Launches with different splits and tile counts back to back on one stream (the
-    arrival counters must be back at zero after each), then the first one again."""
+    """Launches with different splits and tile counts back to back on one stream, combining
+    their parts either way (the arrival counters must be back at zero after each), then
+    the first one again."""
     rng = np.random.default_rng(9450)
     shapes = [(0, 700, 2048, 4, 4), (1, 130, 6144, 8, 2), (0, 700, 2048, 4, 3), (0, 64, 5120, 2, 4),
               (0, 700, 2048, 4, 4)]
@@ -1030,9 +1036,10 @@ def test_gemv_mfma_split_launch_sequence(force):
             y_ref, den = O.gemv(w, layout, n, k, x64(x))
             data[(layout, n, k, batch)] = (dev(w), x.to(DEV).contiguous(), y_ref, den)
     ys = []
-    for layout, n, k, batch, split in shapes:
+    for i, (layout, n, k, batch, split) in enumerate(shapes):  # both ways of combining, alternately
         wd, xd, _, _ = data[(layout, n, k, batch)]
-        ys.append(R.rfp4_gemv(wd, layout, n, k, xd, force=R.make_force("tiles", gemv_splits=split)))
+        ys.append(R.rfp4_gemv(wd, layout, n, k, xd,
+                              force=R.make_force("tiles", gemv_splits=split, gemv_split_combine=i % 2)))
     torch.cuda.synchronize()
     for (layout, n, k, batch, _), y in zip(shapes, ys):
         _, _, y_ref, den = data[(layout, n, k, batch)]
