@@ -20,13 +20,13 @@
 // Activations. The 16 lane groups consume the units of a row in chunks of 16 (chunk
 // t = units 16t .. 16t + 15). Each chunk's activations, for all batch rows, are staged
 // in LDS just before it is multiplied, and so are its weights (each lane stores the
-// unit it loaded and reads back the unit it multiplies); the loads are issued three
+// unit it loaded and reads back the unit it multiplies); the loads are issued two
 // chunks ahead into registers, activations and weights of a chunk together, so that
-// the staging waits only for loads that are due anyway. Per chunk the workgroup reads batch x 16 units of
-// activations from the L2; staging the whole activation matrix up front, or having
-// every lane read its activations from global memory, measured 1.2 to 1.6 times slower.
-// Four wavefronts per workgroup measured faster than 8 or 16 on every decode shape
-// (smaller barriers, registers for three chunks in flight) and faster than 2.
+// the staging waits only for loads that are due anyway. Per chunk the workgroup reads
+// batch x 16 units of activations from the L2; staging the whole activation matrix up
+// front, or having every lane read its activations from global memory, measured 1.2 to
+// 1.6 times slower. Four wavefronts per workgroup measured faster than 8 or 16 on every
+// decode shape (smaller barriers, more registers per wavefront) and faster than 2.
 //
 // Decode. Each workgroup builds a 128-entry LDS table: for every value of a scale byte's
 // low seven bits, the f16 (or bf16) encodings of the eight magnitudes times the decoded

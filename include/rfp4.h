@@ -131,13 +131,14 @@ RFP4_API rfp4_status rfp4_dequant_bf16(const void* w, int layout, int64_t n, int
  *     k = 5120, every matrix's rows a multiple of 16 and at least two 16-row tiles per
  *     CU spread evenly over the CUs (the busiest at most 7 % above the average) run a
  *     batch-1 matrix-core kernel ("tall") instead;
- *   - batch 2: the dot-product kernel when k >= 6144 or the launch has >= 16384 rows
- *     in all, and fewer than 32768 rows; otherwise, like every batch from 3 on, a
- *     matrix-core kernel of 16-row tiles.
- * Workspace: on long rows (at least 12 chunks of 16 units, a unit being two blocks
- * when k / 32 is even and one otherwise) with fewer than four 16-row tiles per CU the
- * tile kernel gives each tile's k range to two workgroups whose fp32 partial sums
- * meet in a device workspace of fixed size (2 MiB + 4 KiB) that the library
+ *   - batch 2: a matrix-core kernel of 16-row tiles when the launch has 4096 to 65536
+ *     rows in all, otherwise the dot-product kernel;
+ *   - batches 3 to 8: the matrix-core kernel, except one matrix of at most 1024 rows
+ *     and k <= 6144 up to batch 6 (the dot-product kernel).
+ * Workspace: when a launch's tiles leave the CUs short of work (long rows: every part
+ * keeps at least 5 chunks of 16 units, a unit being two blocks when k / 32 is even and
+ * one otherwise) the tile kernel gives each tile's k range to 2 to 4 workgroups whose
+ * fp32 partial sums meet in a device workspace of fixed size (2 MiB + 4 KiB) that the library
  * allocates once per (device, stream) at its first need and keeps until the process
  * ends; the parts are added in a fixed order, so results are deterministic. The
  * workspace is never freed or reallocated, and no call synchronizes. It is never
