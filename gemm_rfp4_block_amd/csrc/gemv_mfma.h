@@ -401,10 +401,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     // store of this wavefront has completed, so a part that counts itself has its sums
     // in coherent memory; the combining part's loads are issued only after its counter
     // update, or its poll of the counter, has returned the value that lets them run, so
-    // they read every counted part's sums. A release on the counter and an acquire after it would compile to the
-    // same instructions plus a write-back and an invalidation of the whole L2
-    // (buffer_wbl2 sc1, buffer_inv sc1), which only matter for data written or read
-    // without sc1 (there is none here) and measured 3-5x slower on these launches.
+    // they read every counted part's sums. A release on the counter and an acquire after
+    // it would compile to the same instructions plus a write-back and an invalidation of
+    // the whole L2 (buffer_wbl2 sc1, buffer_inv sc1), which only matter for data written
+    // or read without sc1 (there is none here) and measured 3-5x slower on these launches.
     // Combining. The last part (dispatched last, so normally the last to finish) is the
     // combiner: it polls the arrival counter (a bounded number of times) until the other
     // splits - 1 parts have counted themselves, then reads their sums and adds its own
