@@ -179,6 +179,15 @@ def test_gemv_up_full():
     check_gemv(w, cfg["layout"], cfg["n"], cfg["k"], x)
 
 
+@pytest.mark.parametrize("batch", [2, 4, 8])
+def test_gemv_up_full_batched(batch):
+    """The up-projection weights at batches 2/4/8 on the default path (the matrix-core
+    tile kernel: one tile per workgroup, unsplit), every output against the oracle."""
+    w, _, cfg = synth.gemv_inputs("up")
+    x = synth.activations(np.random.default_rng(9900 + batch), batch, cfg["k"], cfg["xdtype"])
+    check_gemv(w, cfg["layout"], cfg["n"], cfg["k"], x)
+
+
 @pytest.mark.parametrize("batch", [1, 2, 4, 8])
 def test_gemv_down_full_stress(batch):
     w, x, cfg = synth.gemv_inputs("down", batch=batch)
