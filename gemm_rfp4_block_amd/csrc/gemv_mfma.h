@@ -180,20 +180,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
   const int T = (part + 1) * T_all / splits - t_off;
   auto unit_ptr = [&](int q, int t) { return wrow[q] + static_cast<int64_t>(min(G * (t_off + t) + lunit, nu - 1)) * UB; };
 
-  // Decode table (threads 0..127).
-  if (threadIdx.x < 128) {
-    const float sv = scale_exact(threadIdx.x);
-    const float mags[8] = {0.f, 1.f, 2.f, 3.f, 4.f, 6.f, 8.f, 10.f};
-    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t e = M::enc(mags[i] * sv);
-      lo[i >> 2] |= (e & 0xFFu) << (8 * (i & 3));
-      hi[i >> 2] |= (e >> 8) << (8 * (i & 3));
-    }
-    lut[threadIdx.x] = uint4{lo[0], lo[1], hi[0], hi[1]};
-  }
-
   // Activation chunk t: piece i = (b G + u) PU + p is the 16-byte piece p of unit G t + u
   // of activation row b, stored at LDS unit b XROW + u (PU + 1) + p; consecutive threads
   // read consecutive pieces of a row. The loads are clamped to the last piece (and to
@@ -251,6 +237,21 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_kernel(const GemvPa
     xr[d] = x_load(tc);
 #pragma unroll
     for (int q = 0; q < R; ++q) load_unit<LAYOUT, P>(unit_ptr(q, tc), rb[q][d]);
+  }
+
+  // Decode table (threads 0..127), built while the first chunks' loads are in flight
+  // (before them it delayed every workgroup's first request: 1-3 % on most launches).
+  if (threadIdx.x < 128) {
+    const float sv = scale_exact(threadIdx.x);
+    const float mags[8] = {0.f, 1.f, 2.f, 3.f, 4.f, 6.f, 8.f, 10.f};
+    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t e = M::enc(mags[i] * sv);
+      lo[i >> 2] |= (e & 0xFFu) << (8 * (i & 3));
+      hi[i >> 2] |= (e >> 8) << (8 * (i & 3));
+    }
+    lut[threadIdx.x] = uint4{lo[0], lo[1], hi[0], hi[1]};
   }
 
   auto w_store = [&](int d) {
