@@ -246,3 +246,23 @@ def test_sweep_layer_as_the_benchmark_issues_it():
         assert O.normalized_error(sep[j].cpu().numpy(), y_ref, den) <= TOL, synth.SWEEP_SHAPES[j][0]
         yf_ref, fden = (y_ref, den) if x_of[j] == j else O.gemv(w_host, 0, sn, sk, x64(xs[x_of[j]]))
         assert O.normalized_error(fused[j].cpu().numpy(), yf_ref, fden) <= TOL, synth.SWEEP_SHAPES[j][0]
+
+
+@pytest.mark.parametrize("batch", [2, 4])
+@pytest.mark.parametrize("group", ["qkv", "gate_up"])
+def test_fused_decode_launch_batched_default(group, batch):
+    """The fused launches of a decode layer (q + k + v: 8192 rows; gate + up: 34816 rows)
+    at batches 2 and 4 on the default path (the matrix-core tile kernel from batch 2 at
+    these sizes), every output row against the oracle."""
+    idx = {"qkv": [0, 1, 2], "gate_up": [4, 5]}[group]
+    mats = []
+    for j in idx:
+        name, sn, sk = synth.SWEEP_SHAPES[j]
+        mats.append((synth.weights_device(0, sn, sk, 20_000 + j, DEV), sn, sk))
+    k = mats[0][2]
+    x = synth.activations_device(batch, k, "f16", 20_100 + batch, DEV)
+    ys = R.rfp4_gemv_multi([m[0] for m in mats], 0, [m[1] for m in mats], k, x)
+    torch.cuda.synchronize()
+    for (wm, sn, sk), y in zip(mats, ys):
+        y_ref, den = O.gemv(wm.cpu().numpy(), 0, sn, sk, x64(x))
+        assert O.normalized_error(y.cpu().numpy(), y_ref, den) <= TOL
