@@ -225,7 +225,9 @@ typedef struct rfp4_force {
   int32_t gemv_lanes_per_row;  /* dot-product kernel: lanes per weight row, a power of two
                                   from 1 to 64 (0 with gemv_unit_blocks = 0) */
   int32_t gemv_splits;         /* tile kernel: parts of each tile's k range, 1 to 4
-                                  (fewer where a row has fewer chunks); 0 = default */
+                                  (fewer where a row has fewer chunks; launches with two
+                                  tiles per workgroup, batches above 4 on many rows, are
+                                  not split); 0 = default */
   int32_t gemm_plan;           /* rfp4_gemm_plan */
   int32_t gemv_split_combine;  /* tile kernel with a split k range: 0 = the default (the
                                   last part polls, a bounded number of times, until the
