@@ -1250,3 +1250,57 @@ def test_workspace_growth_keeps_captured_graphs_valid():
     assert gemm_error(big_c.to(torch.float64).cpu().numpy(), c_ref, den) <= TOL
     y_ref, vden = O.gemv(big_vw, vl, 1000, vk, x64(big_vx))
     assert O.normalized_error(big_y.cpu().numpy(), y_ref, vden) <= TOL
+
+
+CAPTURE_FIRST_SCRIPT = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import gemm_rfp4_block_amd as R, synth
+import oracle.rfp4_oracle as O
+dev = torch.device("cuda:0")
+rng = np.random.default_rng(9800)
+layout, n, k = 1, 520, 12288  # 33 tiles, 12 chunks per row: two parts from batch 3
+w = synth.weights(rng, layout, n, k)
+wd = torch.from_numpy(w).to(dev)
+x3 = synth.activations(rng, 3, k, "bf16").to(dev).contiguous()
+x8 = synth.activations(rng, 8, k, "bf16").to(dev).contiguous()
+side = torch.cuda.Stream()
+side.wait_stream(torch.cuda.current_stream())
+with torch.cuda.stream(side):
+    R.rfp4_gemv(wd, layout, n, k, x3)  # the stream's workspace, and the batch-3 tile kernel only
+torch.cuda.current_stream().wait_stream(side)
+torch.cuda.synchronize()
+y8 = torch.empty((8, n), dtype=torch.float32, device=dev)
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=side):
+    R.rfp4_gemv(wd, layout, n, k, x8, y=y8)  # first launch of the batch-8 kernel: under capture
+outs = []
+for _ in range(3):
+    y8.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    outs.append(y8.clone())
+eager = R.rfp4_gemv(wd, layout, n, k, x8)
+torch.cuda.synchronize()
+y_ref, den = O.gemv(w, layout, n, k, x8.cpu().double().numpy())
+for o in outs:
+    assert torch.equal(o, outs[0])
+    assert O.normalized_error(o.cpu().numpy(), y_ref, den) <= 2e-3
+assert torch.equal(outs[0], eager), "replay differs from the eager call"
+print("capture-first ok")
+"""
+
+
+def test_first_split_launch_of_a_kernel_under_graph_capture():
+    """In a fresh process, the first launch of a split tile kernel at batch 8 (its
+    occupancy, which the split count depends on, not yet known) happens inside a graph
+    capture on a stream whose split workspace a batch-3 launch has already allocated: the
+    capture succeeds, and every replay gives the eager result bitwise and matches the
+    oracle."""
+    import subprocess
+    import sys
+
+    from tests.conftest import ROOT
+    r = subprocess.run([sys.executable, "-c", CAPTURE_FIRST_SCRIPT, ROOT], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and "capture-first ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
